@@ -1,0 +1,195 @@
+/*
+ * mxq.h - C ABI of the MI355X (gfx950) microscaled-FP4 quantisation library.
+ *
+ * Every entry point takes plain pointers and sizes. Tensor pointers are device
+ * pointers on the current HIP device; `stream` is a hipStream_t (NULL = the null
+ * stream). Calls validate their arguments synchronously, enqueue kernels on
+ * `stream` and return: results are valid once the stream has synchronised. The
+ * caller owns and allocates every buffer; the library allocates no device memory
+ * and keeps no global state. No C++ exception crosses this boundary.
+ *
+ * Layouts. Inputs are row-major [rows, cols] with a row stride `ldx` in elements
+ * (ldx >= cols). Outputs are dense row-major:
+ *   codes   uint8 [rows, cols/2]  two 4-bit codes per byte; element 2j in bits 0-3,
+ *                                 element 2j+1 in bits 4-7
+ *   scales  uint8 [rows, cols/bs] bs = 32 (MXFP4, E8M0 bytes) or 16 (NVFP4, E4M3 bytes)
+ * Column-wise outputs quantise the transpose: codes [cols, rows/2], scales
+ * [cols, rows/bs]; blocks run along rows, as a weight-gradient GEMM consumes them.
+ *
+ * Formats (OCP microscaling layouts):
+ *   E2M1 element   s e1 e0 m: 0, 0.5, 1, 1.5, 2, 3, 4, 6 (and negatives)
+ *   E8M0 scale     2^(byte - 127); 0xFF = NaN
+ *   E4M3 (FP8)     OCP "fn": bias 7, max 448, 0x7F/0xFF = NaN
+ *
+ * Status codes: MXQ_OK on success; MXQ_EINVAL for a NULL pointer, an enum out of
+ * range or a negative size; MXQ_ESHAPE for a dimension that is not a multiple of
+ * the block size (no padding is ever applied) or ldx < cols; MXQ_EALIGN for a
+ * pointer or row stride that breaks the stated alignment; MXQ_EUNSUPPORTED for a
+ * combination not provided; MXQ_EHIP when a launch fails. rows == 0 is a no-op
+ * that returns MXQ_OK. Data-dependent conditions (NaN, Inf, zeros, extreme
+ * exponents) are never errors: they are encoded in the outputs as stated below.
+ *
+ * Sources. The operations follow the text of these pages:
+ *  [HOPPER]  "Practical FP4 Training for Large-Scale MoE Models on Hopper GPUs",
+ *            technical summary: section 1 (MXFP4 = 32-element blocks, E2M1;
+ *            FP8 pipeline = E4M3 with 128-element blocks), section 2B (direct
+ *            FP4 -> FP8 bit remap with hierarchical scale alignment), section 2C
+ *            (fused, ragged, transposed-layout kernels); the Spanish summary,
+ *            section 2 (kernels BF16ToFP4Row / FP4RowToFP8Row / FP4RowToFP8Col,
+ *            subnormal handling, bitwise scale decoding).
+ *  [MI355X]  "Pretraining large language models with MXFP4 on Native FP4
+ *            Hardware": "Qu'est-ce que le MXFP4 ?" (shared E8M0 exponent = the
+ *            block's maximum exponent, elements rounded to nearest) and
+ *            "Expérience d'investigation" (Fprop/Dgrad/Wgrad, deterministic and
+ *            random-sign Hadamard, stochastic rounding).
+ *  [NVFP4]   "Pretraining Large Language Models with NVFP4", technical summary
+ *            section 2A (16-element blocks, E4M3 block scale, fp32 tensor scale)
+ *            and 2B (random Hadamard on Wgrad inputs, stochastic rounding).
+ */
+#ifndef MXQ_H_
+#define MXQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_EINVAL = 1,
+  MXQ_ESHAPE = 2,
+  MXQ_EALIGN = 3,
+  MXQ_EUNSUPPORTED = 4,
+  MXQ_EHIP = 5
+} mxq_status;
+
+typedef enum { MXQ_BF16 = 0, MXQ_F32 = 1 } mxq_dtype;
+typedef enum { MXQ_MXFP4 = 0, MXQ_NVFP4 = 1 } mxq_format;
+typedef enum { MXQ_RNE = 0, MXQ_SR = 1 } mxq_round;
+typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
+
+/*
+ * mxq_quantize - block quantisation of a bf16/fp32 tensor to MXFP4 or NVFP4.
+ *
+ * MXFP4 ([HOPPER] section 1; [MI355X] "Qu'est-ce que le MXFP4 ?"): per block of 32
+ *   E = clamp(floor(log2 max|x|) - 2, -127, 127), stored as the byte E + 127;
+ *   code = sign(x) | E2M1 rounding of |x| / 2^E (nearest, ties to even, saturating
+ *   at 6). A block holding NaN or +-Inf gets scale 0xFF and codes 0; an all-zero
+ *   block gets scale 0 and sign-only codes.
+ * NVFP4 ([NVFP4] section 2A): s_t = RN_fp32(A / 2688) with A = *amax (the tensor's
+ *   max |x|, e.g. from mxq_amax); per block of 16 s_b = E4M3 rounding (nearest
+ *   even, saturating at 448) of the exact quotient max|x_block| / (6 s_t); code =
+ *   sign | E2M1 rounding of the exact quotient |x| / (s_b s_t). s_t == 0 gives
+ *   scale bytes 0 and sign-only codes, a block with s_b == 0 sign-only codes, a
+ *   NaN/Inf amax (or a NaN/Inf block) scale bytes 0x7F and codes 0.
+ * Stochastic rounding (rnd == MXQ_SR; [NVFP4] section 2B, gradients): element n
+ *   (n = sr_offset + its row-major index in the tensor quantised; for column-wise
+ *   outputs the index in the transpose) draws the 32-bit word n mod 4 of
+ *   Philox4x32-10(counter = (n/4 lo, n/4 hi, 0, 0), key = (seed lo, seed hi)); with
+ *   r its top 16 bits, lo the grid value at or below y = |x|/scale and step the gap
+ *   to the next, y rounds up iff y > lo + step (r + 1/2) / 2^16; y >= 6 gives 6.
+ *
+ * x            device, bf16 or fp32 [rows, ldx]; 16-byte aligned, ldx*sizeof a
+ *              multiple of 16 bytes.
+ * axis         MXQ_ROWWISE writes codes_row/scales_row, MXQ_COLWISE codes_col/
+ *              scales_col, MXQ_BOTH both from a single read of x. Unused output
+ *              pointers may be NULL.
+ * amax         NVFP4 only: device fp32[1] holding the tensor amax (read only).
+ * tensor_scale NVFP4 only: device fp32[1] receiving s_t (may be NULL).
+ * Shapes: cols % bs == 0 for row-wise; rows % bs == 0 for column-wise outputs.
+ */
+mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                        mxq_format fmt, mxq_axis axis, mxq_round rnd, uint64_t sr_seed,
+                        uint64_t sr_offset, uint8_t* codes_row, uint8_t* scales_row,
+                        uint8_t* codes_col, uint8_t* scales_col, const float* amax,
+                        float* tensor_scale, void* stream);
+
+/*
+ * mxq_dequantize - codes + scales back to bf16 / fp32 ([HOPPER] Spanish summary
+ * section 2: dequantisation with bitwise scale decoding).
+ * Each output is the exact value v(code) * scale rounded once to the output type
+ * (round to nearest even, overflow to Inf; MXFP4 values with scale bytes <= 252
+ * are always exact). MXFP4: scale = 2^(byte - 127). NVFP4: scale = E4M3(byte) *
+ * (*tensor_scale). A NaN scale gives the quiet NaN 0x7FC0 / 0x7FC00000.
+ * codes [rows, cols/2], scales [rows, cols/bs], y [rows, cols] of out_dt, dense.
+ * tensor_scale: device fp32[1], NVFP4 only. cols % bs == 0.
+ */
+mxq_status mxq_dequantize(const uint8_t* codes, const uint8_t* scales, mxq_format fmt,
+                          int64_t rows, int64_t cols, const float* tensor_scale, void* y,
+                          mxq_dtype out_dt, void* stream);
+
+/*
+ * mxq_fp8_to_mxfp4 - direct FP8 -> MXFP4 quantisation with no bf16 intermediate
+ * ([HOPPER] abstract and section 2B). Input: E4M3 q8 [rows, cols] with one fp32
+ * scale per 1x128 group, s128 [rows, cols/128]; a scale is read through its
+ * exponent field only (2^(field - 127); a power of two is used as is; field 255
+ * makes the group NaN). Output: the MXFP4 quantisation (as mxq_quantize) of the
+ * exact values e4m3(q) * scale: codes [rows, cols/2], e8m0 [rows, cols/32].
+ * cols % 128 == 0. Rows are independent, so ragged per-expert segments are
+ * quantised by one call over their concatenation or by one call per segment with
+ * identical results.
+ */
+mxq_status mxq_fp8_to_mxfp4(const uint8_t* q8, const float* s128, int64_t rows, int64_t cols,
+                            uint8_t* codes, uint8_t* e8m0, void* stream);
+
+/*
+ * mxq_mxfp4_to_fp8 - MXFP4 -> FP8 E4M3 with one scale per 1x128 group
+ * ([HOPPER] section 2B; Spanish summary, FP4RowToFP8Row and subnormal handling).
+ * Per group of four 32-blocks with exponents E_0..E_3: S = max E_j; the fp32
+ * output scale is 2^(S - 127) (byte 0 gives the fp32 subnormal 2^-127); every
+ * element becomes the E4M3 value nearest to v(code) * 2^(E_j - S) (ties to even,
+ * subnormals materialised, sign and -0 kept). Exact whenever the exponents of the
+ * blocks with nonzero codes lie within 8 of each other. A group with a 0xFF
+ * exponent gives scale NaN (0x7FC00000) and codes 0x7F.
+ * codes [rows, cols/2], e8m0 [rows, cols/32] -> q8 [rows, cols], s128 [rows, cols/128].
+ * cols % 128 == 0.
+ */
+mxq_status mxq_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t cols,
+                            uint8_t* q8, float* s128, void* stream);
+
+/*
+ * mxq_rht_quantize - 16-point Hadamard transform fused ahead of quantisation
+ * ([MI355X] "Expérience d'investigation": deterministic H16 and random-sign
+ * Hadamard; [NVFP4] section 2B: random Hadamard on Wgrad inputs).
+ * Every aligned 16-element chunk along the block axis (columns for row-wise
+ * outputs, rows for column-wise outputs) is replaced by y = (1/4) H16 (s * x),
+ * H16 the Sylvester matrix H[i][j] = (-1)^popcount(i & j), s_i = -1 where bit i of
+ * sign_mask is set (sign_mask 0 = deterministic H16). y is computed in fp32
+ * (butterfly stages 1, 2, 4, 8, then the exact scaling by 1/4) and quantised
+ * without an intermediate bf16 rounding. Arguments otherwise as mxq_quantize;
+ * MXFP4 only. rows % 32 == 0 when a column-wise output is requested.
+ */
+mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                            mxq_format fmt, mxq_axis axis, uint32_t sign_mask, mxq_round rnd,
+                            uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
+                            uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                            const float* amax, float* tensor_scale, void* stream);
+
+/*
+ * mxq_rht_apply - the transform alone: y = (1/4) H16 (s * x) on every aligned
+ * 16-chunk of each row, written as fp32 [rows, cols] (dense). cols % 16 == 0.
+ */
+mxq_status mxq_rht_apply(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                         uint32_t sign_mask, float* y, void* stream);
+
+/*
+ * mxq_amax - the tensor amax max|x| that NVFP4's tensor scale needs ([NVFP4]
+ * section 2A). Writes fp32 amax_out[0] (device); a NaN or Inf anywhere gives a
+ * non-finite value (NaN wins over Inf). rows == 0 writes 0.
+ */
+mxq_status mxq_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                    float* amax_out, void* stream);
+
+/* Host helper: the 16-bit sign mask for a seed, bits 0..15 of word 0 of
+ * Philox4x32-10(key = (seed lo, seed hi), counter = 0). */
+uint32_t mxq_rht_signs(uint64_t seed);
+
+/* Host helper: a static, human-readable name for a status code. */
+const char* mxq_status_string(mxq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H_ */

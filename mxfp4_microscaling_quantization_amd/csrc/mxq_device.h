@@ -1,0 +1,266 @@
+// Device-side building blocks shared by the gfx950 kernels: bit views, wave-level
+// reductions, E2M1/E4M3 rounding, Philox4x32-10 and 32-bit division by invariants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// Streaming loads: data is read exactly once, so it is marked non-temporal.
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+__device__ __forceinline__ uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+// DPP quad permutations (64-wide waves are split into quads of 4 lanes).
+constexpr int kQuadSwap1 = 0xB1;  // [1,0,3,2]: exchange with the neighbouring lane
+constexpr int kQuadSwap2 = 0x4E;  // [2,3,0,1]: exchange with the lane two away
+
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, false);
+}
+template <int Ctrl>
+__device__ __forceinline__ float dppf(float v) {
+  return as_f(dpp<Ctrl>(as_u(v)));
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 rounding of a non-negative fp32 magnitude y (exact input, any size).
+// Codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+//
+// Nearest, ties to even, saturating at 6:
+//  * y >= 1: the E2M1 normal range keeps one mantissa bit, so the fp32 mantissa
+//    is rounded at bit 22 (add 0x1FFFFF plus the kept bit, then truncate); the
+//    biased exponent/mantissa pair (t >> 22) is then 254 + code - 2, and anything
+//    past 6.0 (8.0 and up, Inf) clamps to code 7;
+//  * y < 1: E2M1 steps by 0.5 there, which is the fp32 ulp in [2^22, 2^23), so
+//    y + 2^22 is rounded to a multiple of 0.5 by the FPU itself (round to nearest
+//    even), and the distance from 2^22 in ulps is the code (0, 1 or 2).
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+  const uint32_t b = as_u(y);
+  const uint32_t t = b + 0x1FFFFFu + ((b >> 22) & 1u);
+  const uint32_t hi = min(t >> 22, 259u) - 252u;
+  const uint32_t lo = as_u(y + 4194304.0f) - 0x4A800000u;
+  return b >= 0x3F800000u ? hi : lo;
+}
+
+// Largest E2M1 magnitude code whose value is <= y (round toward zero; y >= 0).
+__device__ __forceinline__ uint32_t e2m1_floor(float y) {
+  const uint32_t b = as_u(y);
+  const uint32_t hi = min(b >> 22, 259u) - 252u;
+  const uint32_t lo = y >= 0.5f ? 1u : 0u;
+  return b >= 0x3F800000u ? hi : lo;
+}
+
+// E2M1 magnitude of a code 0..7 as fp32 (0, .5, 1, 1.5, 2, 3, 4, 6).
+__device__ __forceinline__ float e2m1_value(uint32_t m) {
+  const uint32_t normal = (m << 22) + 0x3F000000u;  // m >= 2: exponent/mantissa fields
+  return m >= 2u ? as_f(normal) : (m == 1u ? 0.5f : 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 ("fn") magnitude code k (0..126) -> fp32 value, and nearest-even encoding.
+__device__ __forceinline__ float e4m3_value(uint32_t k) {
+  const uint32_t e = k >> 3, m = k & 7u;
+  return e ? as_f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;  // m * 2^-9
+}
+
+// E4M3 magnitude code of RNE(v) for a finite v >= 0 (exact input), saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t b = as_u(v);
+  if (b >= 0x3C800000u) {  // v >= 2^-6: normal range, keep 3 mantissa bits
+    const uint32_t t = b + 0x7FFFFu + ((b >> 20) & 1u);
+    const uint32_t k = (t >> 20) - (120u << 3);  // (exp - 120) << 3 | mantissa
+    return min(k, 126u);
+  }
+  // subnormal range: multiples of 2^-9; 2^14 has an fp32 ulp of 2^-9
+  return as_u(v + 16384.0f) - 0x46800000u;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): multipliers 0xD2511F53 / 0xCD9E8D57,
+// Weyl key increments 0x9E3779B9 / 0xBB67AE85, ten rounds.
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
+              (uint32_t)p0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Random words of elements n .. n+3 for n a multiple of 4 (one Philox call).
+__device__ __forceinline__ u32x4 philox_words4(uint64_t n, uint64_t seed) {
+  const uint64_t ctr = n >> 2;
+  return philox4x32_10(u32x4{(uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u}, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+// Word of one element n (any n).
+__device__ __forceinline__ uint32_t philox_word(uint64_t n, uint64_t seed) {
+  const u32x4 w = philox_words4(n & ~3ull, seed);
+  const uint32_t s = (uint32_t)(n & 3u);
+  return s == 0 ? w.x : (s == 1 ? w.y : (s == 2 ? w.z : w.w));
+}
+
+// Stochastic E2M1 rounding of an exact fp32 magnitude y with random word u:
+// up iff y > lo + step * (r + 1/2) / 2^16, r = u >> 16; y >= 6 gives 6.
+// lo + step * (r + 1/2) / 2^16 has at most 20 significant bits: exact in fp32.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
+  const uint32_t lo = e2m1_floor(y);
+  const float vlo = e2m1_value(lo);
+  const float step = e2m1_value(lo + 1u) - vlo;
+  const float thr = vlo + step * ((float)(u >> 16) + 0.5f) * (1.0f / 65536.0f);
+  const uint32_t c = (y > thr) ? lo + 1u : lo;
+  return lo >= 7u ? 7u : c;
+}
+
+// ---------------------------------------------------------------------------
+// Unsigned division of i < 2^30 by an invariant d >= 1: q = (i * m) >> s with
+// l = ceil(log2 d), s = 30 + l, m = ceil(2^s / d) < 2^31 + 1.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t i, FastDiv f) {
+  return (uint32_t)(((uint64_t)i * f.m) >> f.s);
+}
+
+}  // namespace mxq
+
+namespace mxq {
+
+// ---------------------------------------------------------------------------
+// NVFP4 two-level scaling with exact-real rounding decisions.
+//
+// The tensor scale s_t = RN_fp32(A / 2688) (IEEE division). All decisions
+// compare an exact quotient with a threshold of few significant bits; they are
+// taken on values normalised by 2^-et (et = floor(log2 s_t)) so that
+// s_t_n = s_t * 2^-et lies in [1, 2) and nothing underflows. A comparison
+// "a >= c * s_t_n" with c exact in fp32 is decided by the sign of
+// fma(c, s_t_n, -a), which is exact.
+struct NvTensor {
+  int mode;     // 0 finite nonzero s_t, 1 s_t == 0, 2 s_t NaN
+  float st;     // s_t as stored
+  float st_n;   // s_t * 2^-et, in [1, 2)
+  int et;
+};
+
+__device__ __forceinline__ NvTensor nv_tensor(float amax) {
+  NvTensor t;
+  const float a = fabsf(amax);
+  t.st = a / 2688.0f;
+  t.et = 0;
+  t.st_n = 1.0f;
+  if (!(a <= 3.40282347e38f)) {  // NaN or Inf
+    t.mode = 2;
+    t.st = __uint_as_float(0x7FC00000u);
+    return t;
+  }
+  if (t.st == 0.0f) {
+    t.mode = 1;
+    return t;
+  }
+  t.mode = 0;
+  int e;
+  const float m = frexpf(t.st, &e);  // st = m * 2^e, m in [0.5, 1)
+  t.st_n = m * 2.0f;
+  t.et = e - 1;
+  return t;
+}
+
+// Exact E4M3 (nearest even, saturating) code of a_n / (6 st_n); a_n >= 0 exact.
+__device__ __forceinline__ uint32_t nv_block_scale(float a_n, float st_n) {
+  const float q = a_n * __builtin_amdgcn_rcpf(6.0f * st_n);
+  uint32_t k = e4m3_rne(q);
+  bool moved = false;
+  if (k < 126u) {
+    const float mu6 = 3.0f * (e4m3_value(k) + e4m3_value(k + 1u));  // 6 * midpoint, exact
+    const float r = fmaf(mu6, st_n, -a_n);
+    if (r < 0.0f || (r == 0.0f && ((k + 1u) & 1u) == 0u)) {
+      k += 1u;
+      moved = true;
+    }
+  }
+  if (!moved && k > 0u) {
+    const float mu6 = 3.0f * (e4m3_value(k - 1u) + e4m3_value(k));
+    const float r = fmaf(mu6, st_n, -a_n);
+    if (r > 0.0f || (r == 0.0f && ((k - 1u) & 1u) == 0u)) k -= 1u;
+  }
+  return k;
+}
+
+// y_a is within a few ulps of a value with at most 3 significant bits (every
+// E2M1 grid value and rounding midpoint is one), at or above 0.2.
+__device__ __forceinline__ bool near_3bit(float y_a) {
+  const uint32_t b = as_u(y_a);
+  return b >= 0x3E4CCCCDu && ((b + 64u) & 0x1FFFFFu) <= 128u;
+}
+
+// Exact nearest-even E2M1 code of x_n / (sb * st_n) by threshold tests.
+__device__ __forceinline__ uint32_t nv_code_exact(float x_n, float sb, float st_n) {
+  uint32_t c = 0;
+  c += fmaf(0.25f * sb, st_n, -x_n) < 0.0f;
+  c += fmaf(0.75f * sb, st_n, -x_n) <= 0.0f;
+  c += fmaf(1.25f * sb, st_n, -x_n) < 0.0f;
+  c += fmaf(1.75f * sb, st_n, -x_n) <= 0.0f;
+  c += fmaf(2.5f * sb, st_n, -x_n) < 0.0f;
+  c += fmaf(3.5f * sb, st_n, -x_n) <= 0.0f;
+  c += fmaf(5.0f * sb, st_n, -x_n) < 0.0f;
+  return c;
+}
+
+// Exact largest code whose value is <= x_n / (sb * st_n).
+__device__ __forceinline__ uint32_t nv_floor_exact(float x_n, float sb, float st_n) {
+  uint32_t c = 0;
+#pragma unroll
+  for (uint32_t m = 1; m < 8; ++m) c += fmaf(e2m1_value(m) * sb, st_n, -x_n) <= 0.0f;
+  return c;
+}
+
+// NVFP4 element code (magnitude) with round-to-nearest-even.
+__device__ __forceinline__ uint32_t nv_code_rne(float x_n, float sb, float inv, float st_n) {
+  const float y = x_n * inv;
+  const uint32_t c = e2m1_rne(y);
+  return near_3bit(y) ? nv_code_exact(x_n, sb, st_n) : c;
+}
+
+// NVFP4 element code (magnitude) with stochastic rounding (word u).
+__device__ __forceinline__ uint32_t nv_code_sr(float x_n, float sb, float inv, float st_n,
+                                               uint32_t u) {
+  const float y = x_n * inv;
+  uint32_t lo = e2m1_floor(y);
+  if (near_3bit(y)) lo = nv_floor_exact(x_n, sb, st_n);
+  if (lo >= 7u) return 7u;
+  const float vlo = e2m1_value(lo);
+  const float step = e2m1_value(lo + 1u) - vlo;
+  const float thr = vlo + step * ((float)(u >> 16) + 0.5f) * (1.0f / 65536.0f);
+  return fmaf(thr * sb, st_n, -x_n) < 0.0f ? lo + 1u : lo;
+}
+
+}  // namespace mxq

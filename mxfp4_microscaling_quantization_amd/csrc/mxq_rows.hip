@@ -1,0 +1,386 @@
+// Row-wise kernels: MXFP4 / NVFP4 quantisation (nearest-even or stochastic, with
+// an optional fused 16-point Hadamard transform along the row), dequantisation,
+// tensor amax, and the stand-alone transform.
+//
+// Work split. A row-major tensor with cols % 8 == 0 is a sequence of 8-element
+// chunks (16 bytes of bf16). Lane t of a 256-thread workgroup takes chunks
+// base + j*256 + t for j < 4, so every load instruction of a wave reads 1 KiB of
+// contiguous bf16 and every code store writes 256 contiguous bytes. A 32-element
+// MXFP4 block spans 4 neighbouring lanes (a DPP quad), a 16-element NVFP4 block or
+// Hadamard chunk spans 2. Output offsets follow from the chunk index alone,
+// because outputs are dense; only the input address needs the row, found by a
+// division by an invariant when rows are strided.
+#include <algorithm>
+
+#include "mxq_blocks.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr uint32_t kChunksPerWG = kThreads * kUnroll;
+
+struct RowParams {
+  const void* x;
+  int64_t ldx;
+  uint32_t chunks;   // 8-element chunks in this slab
+  FastDiv cpr;       // chunks per row
+  uint8_t* codes;
+  uint8_t* scales;
+  uint64_t sr_seed, sr_base;
+  uint32_t sign_mask;
+  const float* amax;
+  float* tensor_scale;
+};
+
+template <bool CONTIG>
+__device__ __forceinline__ size_t in_offset(uint32_t c, const RowParams& p) {
+  if (CONTIG) return (size_t)c * 8;
+  const uint32_t row = fdiv(c, p.cpr);
+  const uint32_t c8 = c - row * p.cpr.d;
+  return (size_t)row * (size_t)p.ldx + (size_t)c8 * 8;
+}
+
+template <typename T, int FMT, bool SR, bool RHT, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
+  const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
+  NvTensor nt;
+  if constexpr (FMT == kNV) {
+    nt = nv_tensor(*p.amax);
+    if (p.tensor_scale && blockIdx.x == 0 && threadIdx.x == 0) *p.tensor_scale = nt.st;
+  }
+  Raw<T> raw[kUnroll];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const uint32_t c = base + j * kThreads;
+    if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), raw[j]);
+    else zero_raw(raw[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const uint32_t c = base + j * kThreads;
+    float v[8];
+    to_f32(raw[j], v);
+    if constexpr (RHT) rht16_pair(v, c & 1u, p.sign_mask);
+    uint32_t u[8];
+    if constexpr (SR) sr_words8(p.sr_base + (uint64_t)c * 8, p.sr_seed, u);
+    uint32_t byte;
+    uint32_t packed;
+    if constexpr (FMT == kMX) packed = mx_encode8<SR>(v, u, byte);
+    else packed = nv_encode8<SR>(v, u, nt, byte);
+    if (c < p.chunks) {
+      reinterpret_cast<uint32_t*>(p.codes)[c] = packed;
+      if constexpr (FMT == kMX) {
+        if ((c & 3u) == 0u) p.scales[c >> 2] = (uint8_t)byte;
+      } else {
+        if ((c & 1u) == 0u) p.scales[c >> 1] = (uint8_t)byte;
+      }
+    }
+  }
+}
+
+template <typename T, int FMT, bool SR, bool RHT>
+static hipError_t launch_rows_t(const RowLaunch& a, hipStream_t st) {
+  // slabs of whole rows with fewer than 2^30 chunks keep every index in 32 bits
+  const int64_t cpr = a.cols / 8;
+  const int64_t max_rows = std::max<int64_t>(1, ((int64_t)1 << 30) / cpr);
+  for (int64_t r0 = 0; r0 < a.rows; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, a.rows - r0);
+    RowParams p;
+    p.x = reinterpret_cast<const T*>(a.x) + r0 * a.ldx;
+    p.ldx = a.ldx;
+    p.chunks = (uint32_t)(nr * cpr);
+    FastDivHost fd = make_fastdiv((uint32_t)cpr);
+    p.cpr = FastDiv{fd.d, fd.m, fd.s};
+    p.codes = a.codes + r0 * (a.cols / 2);
+    const int bs = FMT == kMX ? 32 : 16;
+    p.scales = a.scales + r0 * (a.cols / bs);
+    p.sr_seed = a.sr_seed;
+    p.sr_base = a.sr_base + (uint64_t)(r0 * a.cols);
+    p.sign_mask = a.sign_mask;
+    p.amax = a.amax;
+    p.tensor_scale = r0 == 0 ? a.tensor_scale : nullptr;
+    const uint32_t grid = (p.chunks + kChunksPerWG - 1) / kChunksPerWG;
+    const bool contig = a.ldx == a.cols;
+    if (contig)
+      hipLaunchKernelGGL((quantize_rows_kernel<T, FMT, SR, RHT, true>), dim3(grid), dim3(kThreads), 0,
+                         st, p);
+    else
+      hipLaunchKernelGGL((quantize_rows_kernel<T, FMT, SR, RHT, false>), dim3(grid), dim3(kThreads), 0,
+                         st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int FMT>
+static hipError_t launch_rows_f(const RowLaunch& a, hipStream_t st) {
+  if (a.sr) return a.rht ? launch_rows_t<T, FMT, true, true>(a, st) : launch_rows_t<T, FMT, true, false>(a, st);
+  return a.rht ? launch_rows_t<T, FMT, false, true>(a, st) : launch_rows_t<T, FMT, false, false>(a, st);
+}
+
+hipError_t launch_quantize_rows(const RowLaunch& a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  if (a.dtype == 0)
+    return a.fmt == kMX ? launch_rows_f<uint16_t, kMX>(a, st) : launch_rows_f<uint16_t, kNV>(a, st);
+  return a.fmt == kMX ? launch_rows_f<float, kMX>(a, st) : launch_rows_f<float, kNV>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation. Each lane turns one dword of codes (8 elements) into 8 outputs.
+
+struct DeqParams {
+  const uint32_t* codes;
+  const uint8_t* scales;
+  uint32_t chunks;
+  const float* tensor_scale;
+  void* y;
+};
+
+// RN to bf16 of the exact product a * s_t (a = v * s_b exact, at most 6 bits):
+// the fp32 product is made round-to-odd with the exact fma residual, which makes
+// the second rounding to bf16 a correct single rounding. Products are formed at
+// s_t * 2^k (k = 64 for tiny s_t) so the residual never underflows.
+__device__ __forceinline__ uint32_t bf16_of_product(float a, float st_scaled, int k) {
+  const float p = a * st_scaled;
+  const float r = fmaf(a, st_scaled, -p);
+  uint32_t b = as_u(p);
+  if (r != 0.0f && (b & 1u) == 0u && (b & 0x7FFFFFFFu) != 0u && (b & 0x7FFFFFFFu) < 0x7F800000u) {
+    const bool away = (r > 0.0f) == (p > 0.0f);
+    b = away ? b + 1u : b - 1u;
+  }
+  const uint32_t sign = b & 0x80000000u;
+  uint32_t mag = b & 0x7FFFFFFFu;
+  if (mag >= 0x7F800000u) return (sign >> 16) | 0x7F80u | ((mag > 0x7F800000u) ? 0x40u : 0u);
+  if (k) {
+    const float pm = as_f(mag);
+    if (pm >= 0x1p-62f) {
+      mag -= (uint32_t)k << 23;  // now the unscaled value, a normal fp32
+    } else {
+      // bf16 subnormal: multiples of 2^-133 = 2^-69 in the scaled domain
+      const uint32_t q = (uint32_t)__builtin_rintf(pm * 0x1p69f);
+      return (sign >> 16) | q;
+    }
+  }
+  const uint32_t rnd = mag + 0x7FFFu + ((mag >> 16) & 1u);
+  return (sign >> 16) | (rnd >> 16);
+}
+
+template <int FMT, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
+  const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
+  float st = 0.0f, st_s = 0.0f;
+  int k = 0;
+  if constexpr (FMT == kNV) {
+    st = *p.tensor_scale;
+    k = (fabsf(st) < 0x1p-60f) ? 64 : 0;
+    st_s = ldexpf(st, k);
+  }
+  uint32_t w[kUnroll];
+  uint32_t sb[kUnroll];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const uint32_t c = base + j * kThreads;
+    w[j] = 0;
+    sb[j] = 0;
+    if (c < p.chunks) {
+      w[j] = load_nt(p.codes + c);
+      sb[j] = p.scales[FMT == kMX ? (c >> 2) : (c >> 1)];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const uint32_t c = base + j * kThreads;
+    if (c >= p.chunks) continue;
+    uint32_t out[8];
+    if constexpr (FMT == kMX) {
+      const uint32_t byte = sb[j];
+      const float scale = byte ? as_f(byte << 23) : as_f(0x00400000u);  // 2^(byte-127)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t code = (w[j] >> (4 * i)) & 0xFu;
+        const float v = e2m1_value(code & 7u) * scale;
+        const uint32_t bits = as_u(v) | ((code & 8u) << 28);
+        out[i] = byte == 255u ? 0x7FC00000u : bits;
+        if (!OUT_F32) out[i] >>= 16;
+      }
+    } else {
+      const uint32_t byte = sb[j];
+      const bool nan = (byte & 0x7Fu) == 0x7Fu || !(fabsf(st) <= 3.40282347e38f);
+      const float sbv = as_f(as_u(e4m3_value(byte & 0x7Fu)) | ((byte & 0x80u) << 24));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t code = (w[j] >> (4 * i)) & 0xFu;
+        const float a = as_f(as_u(e2m1_value(code & 7u) * sbv) ^ ((code & 8u) << 28));
+        if (OUT_F32) {
+          out[i] = nan ? 0x7FC00000u : as_u(a * st);
+        } else {
+          out[i] = nan ? 0x7FC0u : bf16_of_product(a, st_s, k);
+        }
+      }
+    }
+    if constexpr (OUT_F32) {
+      float4* y = reinterpret_cast<float4*>(p.y) + (size_t)c * 2;
+      y[0] = make_float4(as_f(out[0]), as_f(out[1]), as_f(out[2]), as_f(out[3]));
+      y[1] = make_float4(as_f(out[4]), as_f(out[5]), as_f(out[6]), as_f(out[7]));
+    } else {
+      uint4 o = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16), out[4] | (out[5] << 16),
+                           out[6] | (out[7] << 16));
+      reinterpret_cast<uint4*>(p.y)[c] = o;
+    }
+  }
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fmt, int64_t rows,
+                             int64_t cols, const float* tensor_scale, void* y, int out_dtype,
+                             hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int64_t cpr = cols / 8;
+  const int64_t max_rows = std::max<int64_t>(1, ((int64_t)1 << 30) / cpr);
+  const int bs = fmt == kMX ? 32 : 16;
+  const size_t osz = out_dtype == 0 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, rows - r0);
+    DeqParams p;
+    p.codes = reinterpret_cast<const uint32_t*>(codes + r0 * (cols / 2));
+    p.scales = scales + r0 * (cols / bs);
+    p.chunks = (uint32_t)(nr * cpr);
+    p.tensor_scale = tensor_scale;
+    p.y = reinterpret_cast<uint8_t*>(y) + (size_t)r0 * cols * osz;
+    const uint32_t grid = (p.chunks + kChunksPerWG - 1) / kChunksPerWG;
+    if (fmt == kMX) {
+      if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kMX, false>), dim3(grid), dim3(kThreads), 0, st, p);
+      else hipLaunchKernelGGL((dequant_kernel<kMX, true>), dim3(grid), dim3(kThreads), 0, st, p);
+    } else {
+      if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kNV, false>), dim3(grid), dim3(kThreads), 0, st, p);
+      else hipLaunchKernelGGL((dequant_kernel<kNV, true>), dim3(grid), dim3(kThreads), 0, st, p);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Tensor amax: a grid-stride pass over 8-element chunks; |x| compared as fp32 bit
+// patterns (NaN > Inf > finite), wave and workgroup reductions, one atomic max
+// per workgroup on a slot the preceding one-thread kernel zeroed.
+
+__global__ void amax_init_kernel(float* out) { *reinterpret_cast<uint32_t*>(out) = 0u; }
+
+template <typename T, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void amax_kernel(RowParams p, uint32_t* out) {
+  const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  uint32_t m = 0;
+  for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < p.chunks; c += gridDim.x * kThreads) {
+    Raw<T> r;
+    load_raw(x, in_offset<CONTIG>(c, p), r);
+    float v[8];
+    to_f32(r, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, as_u(v[i]) & 0x7FFFFFFFu);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) t = max(t, red[i]);
+    atomicMax(out, t);
+  }
+}
+
+hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                       float* amax_out, hipStream_t st) {
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, st, amax_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows == 0) return e;
+  const int64_t cpr = cols / 8;
+  const int64_t max_rows = std::max<int64_t>(1, ((int64_t)1 << 30) / cpr);
+  const size_t esz = dtype == 0 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, rows - r0);
+    RowParams p{};
+    p.x = reinterpret_cast<const uint8_t*>(x) + (size_t)r0 * ldx * esz;
+    p.ldx = ldx;
+    p.chunks = (uint32_t)(nr * cpr);
+    FastDivHost fd = make_fastdiv((uint32_t)cpr);
+    p.cpr = FastDiv{fd.d, fd.m, fd.s};
+    const uint32_t want = (p.chunks + kThreads * 8 - 1) / (kThreads * 8);
+    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 2048));
+    uint32_t* out = reinterpret_cast<uint32_t*>(amax_out);
+    const bool contig = ldx == cols;
+    if (dtype == 0) {
+      if (contig) hipLaunchKernelGGL((amax_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st, p, out);
+      else hipLaunchKernelGGL((amax_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st, p, out);
+    } else {
+      if (contig) hipLaunchKernelGGL((amax_kernel<float, true>), dim3(grid), dim3(kThreads), 0, st, p, out);
+      else hipLaunchKernelGGL((amax_kernel<float, false>), dim3(grid), dim3(kThreads), 0, st, p, out);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// The transform alone, fp32 out.
+
+template <typename T, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void rht_apply_kernel(RowParams p, float* y) {
+  const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const uint32_t c = base + j * kThreads;
+    Raw<T> r;
+    if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), r);
+    else zero_raw(r);
+    float v[8];
+    to_f32(r, v);
+    rht16_pair(v, c & 1u, p.sign_mask);
+    if (c < p.chunks) {
+      float4* o = reinterpret_cast<float4*>(y) + (size_t)c * 2;
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+hipError_t launch_rht_apply(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            uint32_t sign_mask, float* y, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int64_t cpr = cols / 8;
+  const int64_t max_rows = std::max<int64_t>(1, ((int64_t)1 << 30) / cpr);
+  const size_t esz = dtype == 0 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, rows - r0);
+    RowParams p{};
+    p.x = reinterpret_cast<const uint8_t*>(x) + (size_t)r0 * ldx * esz;
+    p.ldx = ldx;
+    p.chunks = (uint32_t)(nr * cpr);
+    FastDivHost fd = make_fastdiv((uint32_t)cpr);
+    p.cpr = FastDiv{fd.d, fd.m, fd.s};
+    p.sign_mask = sign_mask;
+    float* yo = y + (size_t)r0 * cols;
+    const uint32_t grid = (p.chunks + kChunksPerWG - 1) / kChunksPerWG;
+    const bool contig = ldx == cols;
+    if (dtype == 0) {
+      if (contig) hipLaunchKernelGGL((rht_apply_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st, p, yo);
+      else hipLaunchKernelGGL((rht_apply_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st, p, yo);
+    } else {
+      if (contig) hipLaunchKernelGGL((rht_apply_kernel<float, true>), dim3(grid), dim3(kThreads), 0, st, p, yo);
+      else hipLaunchKernelGGL((rht_apply_kernel<float, false>), dim3(grid), dim3(kThreads), 0, st, p, yo);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace mxq

@@ -1,0 +1,284 @@
+// Column-wise (and fused row + column) quantisation from one read of the input.
+//
+// A 256-thread workgroup owns a 128 x 128 tile. Phase 1: every thread loads eight
+// 16-byte chunks (a wave reads four 256-byte row segments per instruction),
+// quantises them row-wise if asked (blocks along the row span a DPP quad, exactly
+// as in the row kernel) and parks the raw values in LDS. Phase 2: thread t owns
+// the column pair 2*(t%64), 2*(t%64)+1 over rows 32*(t/64) .. +31 and reads them as
+// one dword (bf16) per row: a wave's 64 lanes read 64 consecutive dwords of one
+// LDS row, so the column walk is free of bank conflicts without padding. The
+// optional Hadamard transform runs along the rows in registers, each column's 32
+// codes leave as one 16-byte store, and the four row groups of a column land in
+// one contiguous 64-byte run written by the same workgroup.
+#include <algorithm>
+
+#include "mxq_blocks.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+
+constexpr int kTileThreads = 256;
+constexpr int kTileR = 128;
+constexpr int kTileC = 128;
+
+struct TileParams {
+  const void* x;
+  int64_t ldx;
+  int64_t rows, cols;          // slab extent
+  int64_t total_rows;          // whole tensor (column-wise SR index and strides)
+  int64_t row0;                // slab's first row in the whole tensor
+  uint32_t tiles_c;
+  uint32_t sign_mask;
+  uint64_t sr_seed, sr_offset;
+  uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
+  int64_t ld_col_codes, ld_col_scales;
+  const float* amax;
+  float* tensor_scale;
+};
+
+// In-thread Hadamard of 16 values (stages 1, 2, 4, 8, then 1/4); signs by position.
+__device__ __forceinline__ void rht16_local(float* v, uint32_t sign_mask) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = as_f(as_u(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
+}
+
+// MXFP4 encode of 32 values held by one thread; codes into 4 dwords.
+template <bool SR>
+__device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* u, uint32_t out[4]) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
+  const uint32_t ea = am >> 23;
+  const uint32_t byte = ea >= 255u ? 255u : (ea > 2u ? ea - 2u : 0u);
+  const float inv = as_f((254u - min(byte, 252u)) << 23);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = d * 8 + i;
+      const float y = fabsf(v[e]) * inv;
+      uint32_t c = SR ? e2m1_sr(y, u[e]) : e2m1_rne(y);
+      c |= (as_u(v[e]) >> 31) << 3;
+      packed |= c << (4 * i);
+    }
+    out[d] = byte == 255u ? 0u : packed;
+  }
+  return byte;
+}
+
+// NVFP4 encode of one 16-block held by one thread; codes into 2 dwords.
+template <bool SR>
+__device__ __forceinline__ uint32_t nv_encode16(const float* v, const uint32_t* u, const NvTensor& t,
+                                                uint32_t out[2]) {
+  uint32_t am = 0;
+  uint32_t signs[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
+    signs[i >> 3] |= (as_u(v[i]) >> 31) << (4 * (i & 7) + 3);
+  }
+  if (t.mode == 2 || am >= 0x7F800000u) {
+    out[0] = out[1] = 0u;
+    return 0x7Fu;
+  }
+  out[0] = signs[0];
+  out[1] = signs[1];
+  if (t.mode == 1) return 0u;
+  const float a_n = ldexpf(as_f(am), -t.et);
+  const uint32_t k = nv_block_scale(a_n, t.st_n);
+  if (k == 0u) return 0u;
+  const float sb = e4m3_value(k);
+  const float inv = __builtin_amdgcn_rcpf(sb * t.st_n);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float x_n = ldexpf(fabsf(v[i]), -t.et);
+    const uint32_t c = SR ? nv_code_sr(x_n, sb, inv, t.st_n, u[i]) : nv_code_rne(x_n, sb, inv, t.st_n);
+    out[i >> 3] |= c << (4 * (i & 7));
+  }
+  return k;
+}
+
+template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
+__global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams p) {
+  // LDS tile of raw input values, row-major [128][128]
+  __shared__ T tile[kTileR][kTileC];
+  const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  const uint32_t t = threadIdx.x;
+  const uint32_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x - (blockIdx.x / p.tiles_c) * p.tiles_c;
+  const int64_t r0 = (int64_t)tr * kTileR, c0 = (int64_t)tc * kTileC;
+  const int nr = (int)std::min<int64_t>(kTileR, p.rows - r0);
+  const int nc = (int)std::min<int64_t>(kTileC, p.cols - c0);
+  NvTensor nt;
+  if constexpr (FMT == kNV) {
+    nt = nv_tensor(*p.amax);
+    if (p.tensor_scale && blockIdx.x == 0 && t == 0) *p.tensor_scale = nt.st;
+  }
+
+  // ---- phase 1: load (+ row-wise quantise), park raw values in LDS
+  constexpr int kChunks = kTileR * kTileC / 8 / kTileThreads;  // 8 per thread
+  Raw<T> raw[kChunks];
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const uint32_t q = t + j * kTileThreads;
+    const int row = (int)(q >> 4), cc = (int)(q & 15u);
+    if (row < nr && cc * 8 < nc) load_raw(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, raw[j]);
+    else zero_raw(raw[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kChunks; ++j) {
+    const uint32_t q = t + j * kTileThreads;
+    const int row = (int)(q >> 4), cc = (int)(q & 15u);
+    *reinterpret_cast<Raw<T>*>(&tile[row][cc * 8]) = raw[j];
+    if constexpr (ROW) {
+      float v[8];
+      to_f32(raw[j], v);
+      if constexpr (RHT) rht16_pair(v, cc & 1, p.sign_mask);
+      uint32_t u[8];
+      const int64_t grow = p.row0 + r0 + row;
+      const int64_t col = c0 + cc * 8;
+      if constexpr (SR) sr_words8(p.sr_offset + (uint64_t)(grow * p.cols + col), p.sr_seed, u);
+      uint32_t byte, packed;
+      if constexpr (FMT == kMX) packed = mx_encode8<SR>(v, u, byte);
+      else packed = nv_encode8<SR>(v, u, nt, byte);
+      if (row < nr && cc * 8 < nc) {
+        const int64_t lr = r0 + row;  // row within the slab
+        *reinterpret_cast<uint32_t*>(p.codes_row + (lr * p.cols + col) / 2) = packed;
+        constexpr int bs = FMT == kMX ? 32 : 16;
+        if (col % bs == 0) p.scales_row[lr * (p.cols / bs) + col / bs] = (uint8_t)byte;
+      }
+    }
+  }
+  if constexpr (!COL) return;
+  __syncthreads();
+
+  // ---- phase 2: column pairs over 32 rows
+  const int cp = (int)(t & 63u);
+  const int h = (int)(t >> 6);
+  float v0[32], v1[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][cp * 2]);
+      v0[i] = as_f(w << 16);
+      v1[i] = as_f(w & 0xFFFF0000u);
+    } else {
+      const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][cp * 2]);
+      v0[i] = w.x;
+      v1[i] = w.y;
+    }
+  }
+  if constexpr (RHT) {
+    rht16_local(v0, p.sign_mask);
+    rht16_local(v0 + 16, p.sign_mask);
+    rht16_local(v1, p.sign_mask);
+    rht16_local(v1 + 16, p.sign_mask);
+  }
+  const int vrows = nr - h * 32;  // valid rows of this 32-row group
+  if (vrows <= 0) return;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float* v = k ? v1 : v0;
+    const int64_t col = c0 + cp * 2 + k;
+    if (col >= c0 + nc) continue;
+    const int64_t grow0 = p.row0 + r0 + h * 32;  // first row of the group in the whole tensor
+    uint32_t u[32];
+    if constexpr (SR) {
+      const uint64_t n0 = p.sr_offset + (uint64_t)(col * p.total_rows + grow0);
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const u32x4 w = philox_words4(n0 + i, p.sr_seed);
+        u[i] = w.x; u[i + 1] = w.y; u[i + 2] = w.z; u[i + 3] = w.w;
+      }
+    }
+    uint8_t* cdst = p.codes_col + col * p.ld_col_codes + grow0 / 2;
+    uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
+    if constexpr (FMT == kMX) {
+      uint32_t out[4];
+      const uint32_t byte = mx_encode32<SR>(v, u, out);
+      *reinterpret_cast<uint4*>(cdst) = make_uint4(out[0], out[1], out[2], out[3]);
+      sdst[grow0 / 32] = (uint8_t)byte;
+    } else {
+      uint32_t out[4];
+      const uint32_t b0 = nv_encode16<SR>(v, u, nt, out);
+      const uint32_t b1 = nv_encode16<SR>(v + 16, u + 16, nt, out + 2);
+      // 8-byte stores: rows % 16 == 0 only guarantees 8-byte aligned column runs
+      *reinterpret_cast<uint2*>(cdst) = make_uint2(out[0], out[1]);
+      sdst[grow0 / 16] = (uint8_t)b0;
+      if (vrows >= 32) {
+        *reinterpret_cast<uint2*>(cdst + 8) = make_uint2(out[2], out[3]);
+        sdst[grow0 / 16 + 1] = (uint8_t)b1;
+      }
+    }
+  }
+}
+
+template <typename T, int FMT, bool SR, bool RHT>
+static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
+  // slabs keep the tile count of one launch well inside the grid limit
+  const int64_t max_rows = (int64_t)kTileR * 65536;
+  for (int64_t s0 = 0; s0 < a.rows; s0 += max_rows) {
+    const int64_t nr = std::min(max_rows, a.rows - s0);
+    TileParams p;
+    const size_t esz = sizeof(T);
+    p.x = reinterpret_cast<const uint8_t*>(a.x) + (size_t)s0 * a.ldx * esz;
+    p.ldx = a.ldx;
+    p.rows = nr;
+    p.cols = a.cols;
+    p.total_rows = a.total_rows;
+    p.row0 = a.row0 + s0;
+    const int64_t tiles_r = (nr + kTileR - 1) / kTileR;
+    const int64_t tiles_c = (a.cols + kTileC - 1) / kTileC;
+    p.tiles_c = (uint32_t)tiles_c;
+    p.sign_mask = a.sign_mask;
+    p.sr_seed = a.sr_seed;
+    p.sr_offset = a.sr_offset;
+    const int bs = FMT == kMX ? 32 : 16;
+    p.codes_row = a.codes_row ? a.codes_row + s0 * (a.cols / 2) : nullptr;
+    p.scales_row = a.scales_row ? a.scales_row + s0 * (a.cols / bs) : nullptr;
+    p.codes_col = a.codes_col;
+    p.scales_col = a.scales_col;
+    p.ld_col_codes = a.ld_col_codes;
+    p.ld_col_scales = a.ld_col_scales;
+    p.amax = a.amax;
+    p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
+    const uint32_t grid = (uint32_t)(tiles_r * tiles_c);
+    if (a.want_row && a.want_col)
+      hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, true, true>), dim3(grid),
+                         dim3(kTileThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, false, true>), dim3(grid),
+                         dim3(kTileThreads), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int FMT>
+static hipError_t launch_tiles_f(const TileLaunch& a, hipStream_t st) {
+  if (a.sr) return a.rht ? launch_tiles_t<T, FMT, true, true>(a, st) : launch_tiles_t<T, FMT, true, false>(a, st);
+  return a.rht ? launch_tiles_t<T, FMT, false, true>(a, st) : launch_tiles_t<T, FMT, false, false>(a, st);
+}
+
+hipError_t launch_quantize_tiles(const TileLaunch& a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  if (a.dtype == 0)
+    return a.fmt == kMX ? launch_tiles_f<uint16_t, kMX>(a, st) : launch_tiles_f<uint16_t, kNV>(a, st);
+  return a.fmt == kMX ? launch_tiles_f<float, kMX>(a, st) : launch_tiles_f<float, kNV>(a, st);
+}
+
+}  // namespace mxq

@@ -1,0 +1,87 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point the
+header declares, rejects invalid arguments before touching the GPU, and its host
+helpers agree with the oracle. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_microscaling_quantization_amd import mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mxq_status|uint32_t|const char\*)\s+(mxq_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) == 9
+    L = mxq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(6):
+        assert mxq.mxq_status_string(s).startswith("MXQ_")
+    assert "unknown" in mxq.mxq_status_string(99)
+
+
+def test_rht_signs_match_oracle():
+    from oracle import rht
+    for seed in (0, 1, 4, 7, 2 ** 40 + 3, 2 ** 64 - 1):
+        assert mxq.mxq_rht_signs(seed) == rht.sign_mask_from_seed(seed)
+
+
+FAKE = 0x10000  # a 16-byte aligned, never dereferenced address
+
+
+def q(**kw):
+    a = dict(x=FAKE, dt=0, rows=64, cols=64, ldx=64, fmt=0, axis=1, rnd=0, seed=0, off=0,
+             cr=FAKE, sr=FAKE, cc=FAKE, sc=FAKE, amax=FAKE, ts=None, stream=None)
+    a.update(kw)
+    return mxq.lib().mxq_quantize(a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["fmt"], a["axis"],
+                                  a["rnd"], a["seed"], a["off"], a["cr"], a["sr"], a["cc"], a["sc"],
+                                  a["amax"], a["ts"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mxq.MXQ_EINVAL),
+    (dict(dt=2), mxq.MXQ_EINVAL),
+    (dict(fmt=5), mxq.MXQ_EINVAL),
+    (dict(axis=0), mxq.MXQ_EINVAL),
+    (dict(rnd=3), mxq.MXQ_EINVAL),
+    (dict(rows=-1), mxq.MXQ_EINVAL),
+    (dict(cr=None), mxq.MXQ_EINVAL),
+    (dict(axis=2, sc=None), mxq.MXQ_EINVAL),
+    (dict(fmt=1, amax=None), mxq.MXQ_EINVAL),
+    (dict(cols=48), mxq.MXQ_ESHAPE),             # not a multiple of 32
+    (dict(ldx=32), mxq.MXQ_ESHAPE),
+    (dict(axis=2, rows=48), mxq.MXQ_ESHAPE),
+    (dict(x=FAKE + 8), mxq.MXQ_EALIGN),
+    (dict(ldx=68), mxq.MXQ_EALIGN),              # 136-byte rows
+    (dict(cr=FAKE + 4), mxq.MXQ_EALIGN),
+    (dict(rows=0, x=None), mxq.MXQ_OK),
+])
+def test_quantize_validation(kw, status):
+    assert q(**kw) == status
+
+
+def test_other_entry_points_validation():
+    L = mxq.lib()
+    assert L.mxq_dequantize(FAKE, FAKE, 0, 4, 48, None, FAKE, 0, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_dequantize(FAKE, FAKE, 1, 4, 64, None, FAKE, 0, None) == mxq.MXQ_EINVAL
+    assert L.mxq_dequantize(FAKE, FAKE, 0, 4, 64, None, FAKE + 2, 0, None) == mxq.MXQ_EALIGN
+    assert L.mxq_fp8_to_mxfp4(FAKE, FAKE, 4, 96, FAKE, FAKE, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_fp8_to_mxfp4(None, FAKE, 4, 128, FAKE, FAKE, None) == mxq.MXQ_EINVAL
+    assert L.mxq_mxfp4_to_fp8(FAKE, FAKE + 1, 4, 128, FAKE, FAKE, None) == mxq.MXQ_EALIGN
+    assert L.mxq_mxfp4_to_fp8(FAKE, FAKE, 0, 128, FAKE, FAKE, None) == mxq.MXQ_OK
+    assert L.mxq_rht_apply(FAKE, 0, 4, 40, 40, 0, FAKE, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_rht_quantize(FAKE, 0, 4, 64, 64, 1, 1, 0, 0, 0, 0, FAKE, FAKE, None, None, FAKE, FAKE,
+                              None) == mxq.MXQ_EUNSUPPORTED
+    assert L.mxq_amax(FAKE, 0, 4, 64, 64, None, None) == mxq.MXQ_EINVAL
