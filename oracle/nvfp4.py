@@ -10,7 +10,7 @@ applied on top of the block scale. Stochastic rounding is used for gradients
 Readings (the pages give no formulas):
   N1 the tensor scale is s_t = RN_fp32(A / (6 * 448)) with A = max |x| over the
      tensor, so the largest block scale lands on 448, the largest E4M3 value;
-     A = 0 gives s_t = 0; a NaN or Inf anywhere gives s_t = NaN.
+     A = 0 gives s_t = 0; a NaN or Inf anywhere makes A non-finite and s_t NaN.
   N2 the block scale is s_b = RNE_E4M3(a_b / (6 * s_t)) with a_b = max |x| over the
      block, the quotient taken exactly and rounded once (ties to even, saturating
      at 448).
@@ -46,11 +46,11 @@ NV_TENSOR_DIVISOR = 6.0 * 448.0  # 2688
 
 
 def tensor_amax(x: np.ndarray) -> float:
-    """A = max |x|; NaN if any element is NaN or Inf."""
+    """A = max |x| over the tensor: +Inf if an infinity is present, NaN if a NaN is."""
     x = np.asarray(x, dtype=np.float64)
     if x.size == 0:
         return 0.0
-    if not np.isfinite(x).all():
+    if np.isnan(x).any():
         return float("nan")
     return float(np.abs(x).max())
 
