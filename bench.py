@@ -166,6 +166,20 @@ def main() -> int:
         per[name] = {"us": round(us, 3), "bytes": b, "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         print(f"[bench] {name:20s} {us:9.2f} us  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of 8 TB/s",
               file=sys.stderr, flush=True)
+    # reference: a device-to-device copy of 1 GiB (read + write bytes)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
+    print(f"[bench] torch D2D copy of 1 GiB: {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
     dom = max(per, key=lambda k: per[k]["us"])
     roof = {"kernel": dom, "bound": "hbm", "achieved": per[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(per[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
@@ -196,6 +210,7 @@ def main() -> int:
                                "all eight quantise/convert kernels per step",
                    "rows": R, "cols": C, "elements_per_step": R * C, "bytes_per_step": step_bytes},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "copy_reference_GB_s": round(copy_gbs, 1),
         "per_kernel": per,
         "roofline": roof,
         "cpu_baseline": cpu,

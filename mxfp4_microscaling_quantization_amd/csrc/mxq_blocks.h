@@ -72,10 +72,7 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t half, uint32_t s
 }
 
 __device__ __forceinline__ void sr_words8(uint64_t n, uint64_t seed, uint32_t u[8]) {
-  const u32x4 a = philox_words4(n, seed);
-  const u32x4 b = philox_words4(n + 4, seed);
-  u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
-  u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
+  philox_words<8>(n, seed, u);
 }
 
 // MXFP4: 8 values of one lane (a quarter of a 32-block) -> 8 codes, block byte.
@@ -89,15 +86,33 @@ __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t 
   am = max(am, dpp<kQuadSwap2>(am));
   const uint32_t ea = am >> 23;  // 255: NaN or Inf in the block
   byte = ea >= 255u ? 255u : (ea > 2u ? ea - 2u : 0u);
-  const float inv = as_f((254u - min(byte, 252u)) << 23);  // 2^-E
   uint32_t packed = 0;
+  if constexpr (SR) {
+    const float inv = as_f((254u - min(byte, 252u)) << 23);  // 2^-E
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float y = fabsf(v[i]) * inv;
-    uint32_t c = SR ? e2m1_sr(y, u[i]) : e2m1_rne(y);
-    c |= (as_u(v[i]) >> 31) << 3;
-    packed |= c << (4 * i);
+    for (int i = 0; i < 8; ++i) {
+      const float y = fabsf(v[i]) * inv;
+      const uint32_t c = e2m1_sr(y, u[i]) | ((as_u(v[i]) >> 31) << 3);
+      packed |= c << (4 * i);
+    }
+  } else {
+    packed = fp4x8_from_f32(v, e8m0_operand(min(byte, 254u)));
   }
+  return byte == 255u ? 0u : packed;
+}
+
+// MXFP4 round-to-nearest-even of 8 raw bf16 values (4 dwords): integer amax on the
+// magnitude halves, then four hardware conversions.
+__device__ __forceinline__ uint32_t mx_encode8_bf16(const uint4& r, uint32_t& byte) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  m = max(m, dpp<kQuadSwap1>(m));
+  m = max(m, dpp<kQuadSwap2>(m));
+  const uint32_t ea = m >> 7;  // bf16 exponent field of the block amax; 255: NaN/Inf
+  byte = ea >= 255u ? 255u : (ea > 2u ? ea - 2u : 0u);
+  const uint32_t packed = fp4x8_from_bf16(w, e8m0_operand(min(byte, 254u)));
   return byte == 255u ? 0u : packed;
 }
 
@@ -124,16 +139,8 @@ __device__ __forceinline__ uint32_t nv_encode8(const float v[8], const uint32_t 
   const uint32_t k = nv_block_scale(a_n, t.st_n);
   byte = k;
   if (k == 0u) return signs;
-  const float sb = e4m3_value(k);
-  const float inv = __builtin_amdgcn_rcpf(sb * t.st_n);
-  uint32_t packed = signs;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x_n = ldexpf(fabsf(v[i]), -t.et);
-    const uint32_t c = SR ? nv_code_sr(x_n, sb, inv, t.st_n, u[i]) : nv_code_rne(x_n, sb, inv, t.st_n);
-    packed |= c << (4 * i);
-  }
-  return packed;
+  if constexpr (SR) return nv_codes8_sr(v, u, t, k);
+  return nv_codes8_rne(v, t, k);
 }
 
 }  // namespace mxq

@@ -42,6 +42,36 @@ __device__ __forceinline__ float dppf(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// gfx950 scaled FP4 conversions. With the scale operand holding an E8M0 byte b in
+// its exponent field (as_f(b << 23); b = 0 stands for 2^-127), the down-conversion
+// returns sign | nearest-even E2M1 of |x| / 2^(b-127), saturating at 6, and the
+// up-conversion returns v(code) * 2^(b-127) rounded to the output type. Checked
+// against the oracle for every bf16 input and every b in 0..254; non-finite
+// inputs are never passed (NaN blocks are overwritten by the callers).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float e8m0_operand(uint32_t byte) { return as_f(byte << 23); }
+
+// Four bf16 pairs (dwords) -> 8 codes in one dword, element 2j in the low nibble.
+__device__ __forceinline__ uint32_t fp4x8_from_bf16(const uint32_t w[4], float scale) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2_t, w[0]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[1]), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[2]), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, w[3]), scale, 3);
+  return r;
+}
+
+// Eight fp32 values -> 8 codes in one dword.
+__device__ __forceinline__ uint32_t fp4x8_from_f32(const float* v, float scale) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // E2M1 rounding of a non-negative fp32 magnitude y (exact input, any size).
 // Codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 //
@@ -119,6 +149,38 @@ __device__ __forceinline__ u32x4 philox_words4(uint64_t n, uint64_t seed) {
   const uint64_t ctr = n >> 2;
   return philox4x32_10(u32x4{(uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u}, (uint32_t)seed,
                        (uint32_t)(seed >> 32));
+}
+
+// Random words of elements n .. n+K-1 for any n (K a multiple of 4): K/4 Philox
+// calls when n is a multiple of 4, one more otherwise. n mod 4 is the same for
+// every lane of a launch, so the shift below is a uniform branch.
+template <int K>
+__device__ __forceinline__ void philox_words(uint64_t n, uint64_t seed, uint32_t* u) {
+  const uint32_t s = (uint32_t)(n & 3u);
+  const uint64_t b = n - s;
+  uint32_t w[K + 4];
+#pragma unroll
+  for (int i = 0; i < K; i += 4) {
+    const u32x4 a = philox_words4(b + i, seed);
+    w[i] = a.x; w[i + 1] = a.y; w[i + 2] = a.z; w[i + 3] = a.w;
+  }
+  if (s == 0) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) u[i] = w[i];
+    return;
+  }
+  const u32x4 a = philox_words4(b + K, seed);
+  w[K] = a.x; w[K + 1] = a.y; w[K + 2] = a.z; w[K + 3] = a.w;
+  if (s == 1) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) u[i] = w[i + 1];
+  } else if (s == 2) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) u[i] = w[i + 2];
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) u[i] = w[i + 3];
+  }
 }
 
 // Word of one element n (any n).
@@ -261,6 +323,74 @@ __device__ __forceinline__ uint32_t nv_code_sr(float x_n, float sb, float inv, f
   const float step = e2m1_value(lo + 1u) - vlo;
   const float thr = vlo + step * ((float)(u >> 16) + 0.5f) * (1.0f / 65536.0f);
   return fmaf(thr * sb, st_n, -x_n) < 0.0f ? lo + 1u : lo;
+}
+
+// Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1.
+// Nearest even: the quotient is approximated in fp32 and rounded by the hardware
+// conversion; values that land within 64 ulp of a value with 3 significant bits
+// (every rounding midpoint is one) are decided again exactly. When s_t >= 2^-80
+// the exact tests use s_t itself (no product underflows), else normalised values.
+__device__ __forceinline__ uint32_t nv_codes8_rne(const float* v, const NvTensor& t, uint32_t k) {
+  const float sb = e4m3_value(k);
+  const float r = __builtin_amdgcn_rcpf(sb * t.st_n);
+  uint32_t packed = 0;
+  if (t.et >= -80) {
+    const float inv = ldexpf(r, -t.et);
+    float y[8];
+    uint32_t flag = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      y[i] = v[i] * inv;
+      flag |= (uint32_t)near_3bit(fabsf(y[i])) << i;
+    }
+    packed = fp4x8_from_f32(y, 1.0f);
+    if (flag) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((flag >> i) & 1u) {
+          const uint32_t c = nv_code_exact(fabsf(v[i]), sb, t.st) | ((as_u(v[i]) >> 31) << 3);
+          packed = (packed & ~(0xFu << (4 * i))) | (c << (4 * i));
+        }
+      }
+    }
+    return packed;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x_n = ldexpf(fabsf(v[i]), -t.et);
+    const uint32_t c = nv_code_rne(x_n, sb, r, t.st_n) | ((as_u(v[i]) >> 31) << 3);
+    packed |= c << (4 * i);
+  }
+  return packed;
+}
+
+// Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1,
+// stochastic rounding with words u.
+__device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t* u, const NvTensor& t,
+                                                 uint32_t k) {
+  const float sb = e4m3_value(k);
+  const float r = __builtin_amdgcn_rcpf(sb * t.st_n);
+  const bool fast = t.et >= -80;
+  const float inv = fast ? ldexpf(r, -t.et) : r;
+  const float sts = fast ? t.st : t.st_n;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float ax = fabsf(v[i]);
+    const float xs = fast ? ax : ldexpf(ax, -t.et);
+    const float y = xs * inv;
+    uint32_t lo = e2m1_floor(y);
+    if (near_3bit(y)) lo = nv_floor_exact(xs, sb, sts);
+    uint32_t c = 7u;
+    if (lo < 7u) {
+      const float vlo = e2m1_value(lo);
+      const float step = e2m1_value(lo + 1u) - vlo;
+      const float thr = vlo + step * ((float)(u[i] >> 16) + 0.5f) * (1.0f / 65536.0f);
+      c = fmaf(thr * sb, sts, -xs) < 0.0f ? lo + 1u : lo;
+    }
+    packed |= (c | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+  }
+  return packed;
 }
 
 }  // namespace mxq

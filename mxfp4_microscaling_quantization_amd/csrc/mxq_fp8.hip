@@ -71,14 +71,29 @@ __global__ __launch_bounds__(kF8Threads) void fp8_to_mxfp4_kernel(F8Params p) {
       byte = (uint32_t)(E + 127);
       D = std::min(126, std::max(-126, sexp - 127 - E));
     }
-    const float f = as_f((uint32_t)(127 + D) << 23);  // 2^D
     uint32_t out[2] = {0u, 0u};
+    // the conversion divides by 2^(sb - 127): sb = E - (sexp - 127) + 127 = 127 - D
+    const int sb = 127 - D;
+    if (sb >= 0 && sb <= 254) {
+      float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t b = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      const float y = e4m3_value(b & 0x7Fu) * f;
-      const uint32_t code = e2m1_rne(y) | ((b >> 7) << 3);
-      out[i >> 3] |= code << (4 * (i & 7));
+      for (int i = 0; i < 4; ++i) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+        v[4 * i] = lo.x; v[4 * i + 1] = lo.y; v[4 * i + 2] = hi.x; v[4 * i + 3] = hi.y;
+      }
+      const float scale = e8m0_operand((uint32_t)sb);
+      out[0] = fp4x8_from_f32(v, scale);
+      out[1] = fp4x8_from_f32(v + 8, scale);
+    } else {  // exponents beyond the conversion's scale range: ALU rounding
+      const float f = as_f((uint32_t)(127 + D) << 23);  // 2^D
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t b = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const float y = e4m3_value(b & 0x7Fu) * f;
+        const uint32_t code = e2m1_rne(y) | ((b >> 7) << 3);
+        out[i >> 3] |= code << (4 * (i & 7));
+      }
     }
     if (byte == 255u) out[0] = out[1] = 0u;
     if (c < p.chunks) {

@@ -61,15 +61,19 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
 #pragma unroll
   for (int j = 0; j < kUnroll; ++j) {
     const uint32_t c = base + j * kThreads;
-    float v[8];
-    to_f32(raw[j], v);
-    if constexpr (RHT) rht16_pair(v, c & 1u, p.sign_mask);
-    uint32_t u[8];
-    if constexpr (SR) sr_words8(p.sr_base + (uint64_t)c * 8, p.sr_seed, u);
     uint32_t byte;
     uint32_t packed;
-    if constexpr (FMT == kMX) packed = mx_encode8<SR>(v, u, byte);
-    else packed = nv_encode8<SR>(v, u, nt, byte);
+    if constexpr (FMT == kMX && !SR && !RHT && sizeof(T) == 2) {
+      packed = mx_encode8_bf16(raw[j].w, byte);
+    } else {
+      float v[8];
+      to_f32(raw[j], v);
+      if constexpr (RHT) rht16_pair(v, c & 1u, p.sign_mask);
+      uint32_t u[8];
+      if constexpr (SR) sr_words8(p.sr_base + (uint64_t)c * 8, p.sr_seed, u);
+      if constexpr (FMT == kMX) packed = mx_encode8<SR>(v, u, byte);
+      else packed = nv_encode8<SR>(v, u, nt, byte);
+    }
     if (c < p.chunks) {
       reinterpret_cast<uint32_t*>(p.codes)[c] = packed;
       if constexpr (FMT == kMX) {
@@ -198,14 +202,26 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
     uint32_t out[8];
     if constexpr (FMT == kMX) {
       const uint32_t byte = sb[j];
-      const float scale = byte ? as_f(byte << 23) : as_f(0x00400000u);  // 2^(byte-127)
+      const float scale = e8m0_operand(min(byte, 254u));
+      const bool nan = byte == 255u;
+      if constexpr (OUT_F32) {
+        const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 0);
+        const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 1);
+        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 2);
+        const f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 3);
+        const float vv[8] = {a.x, a.y, b.x, b.y, d.x, d.y, e.x, e.y};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t code = (w[j] >> (4 * i)) & 0xFu;
-        const float v = e2m1_value(code & 7u) * scale;
-        const uint32_t bits = as_u(v) | ((code & 8u) << 28);
-        out[i] = byte == 255u ? 0x7FC00000u : bits;
-        if (!OUT_F32) out[i] >>= 16;
+        for (int i = 0; i < 8; ++i) out[i] = nan ? 0x7FC00000u : as_u(vv[i]);
+      } else {
+        uint32_t o[4];
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 3));
+        uint4 ov = nan ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u)
+                       : make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4*>(p.y)[c] = ov;
+        continue;
       }
     } else {
       const uint32_t byte = sb[j];
@@ -275,13 +291,22 @@ template <typename T, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void amax_kernel(RowParams p, uint32_t* out) {
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   uint32_t m = 0;
-  for (uint32_t c = blockIdx.x * kThreads + threadIdx.x; c < p.chunks; c += gridDim.x * kThreads) {
-    Raw<T> r;
-    load_raw(x, in_offset<CONTIG>(c, p), r);
-    float v[8];
-    to_f32(r, v);
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < p.chunks; c0 += stride * kUnroll) {
+    Raw<T> r[kUnroll];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, as_u(v[i]) & 0x7FFFFFFFu);
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint32_t c = c0 + j * stride;
+      if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), r[j]);
+      else zero_raw(r[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      float v[8];
+      to_f32(r[j], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = max(m, as_u(v[i]) & 0x7FFFFFFFu);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
@@ -311,8 +336,8 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
     p.chunks = (uint32_t)(nr * cpr);
     FastDivHost fd = make_fastdiv((uint32_t)cpr);
     p.cpr = FastDiv{fd.d, fd.m, fd.s};
-    const uint32_t want = (p.chunks + kThreads * 8 - 1) / (kThreads * 8);
-    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 2048));
+    const uint32_t want = (p.chunks + kThreads * 4 * kUnroll - 1) / (kThreads * 4 * kUnroll);
+    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 4096));
     uint32_t* out = reinterpret_cast<uint32_t*>(amax_out);
     const bool contig = ldx == cols;
     if (dtype == 0) {

@@ -63,19 +63,24 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* 
   for (int i = 0; i < 32; ++i) am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
   const uint32_t ea = am >> 23;
   const uint32_t byte = ea >= 255u ? 255u : (ea > 2u ? ea - 2u : 0u);
-  const float inv = as_f((254u - min(byte, 252u)) << 23);
+  if constexpr (SR) {
+    const float inv = as_f((254u - min(byte, 252u)) << 23);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    uint32_t packed = 0;
+    for (int d = 0; d < 4; ++d) {
+      uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = d * 8 + i;
-      const float y = fabsf(v[e]) * inv;
-      uint32_t c = SR ? e2m1_sr(y, u[e]) : e2m1_rne(y);
-      c |= (as_u(v[e]) >> 31) << 3;
-      packed |= c << (4 * i);
+      for (int i = 0; i < 8; ++i) {
+        const int e = d * 8 + i;
+        const float y = fabsf(v[e]) * inv;
+        const uint32_t c = e2m1_sr(y, u[e]) | ((as_u(v[e]) >> 31) << 3);
+        packed |= c << (4 * i);
+      }
+      out[d] = byte == 255u ? 0u : packed;
     }
-    out[d] = byte == 255u ? 0u : packed;
+  } else {
+    const float scale = e8m0_operand(min(byte, 254u));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) out[d] = byte == 255u ? 0u : fp4x8_from_f32(v + 8 * d, scale);
   }
   return byte;
 }
@@ -101,13 +106,12 @@ __device__ __forceinline__ uint32_t nv_encode16(const float* v, const uint32_t* 
   const float a_n = ldexpf(as_f(am), -t.et);
   const uint32_t k = nv_block_scale(a_n, t.st_n);
   if (k == 0u) return 0u;
-  const float sb = e4m3_value(k);
-  const float inv = __builtin_amdgcn_rcpf(sb * t.st_n);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float x_n = ldexpf(fabsf(v[i]), -t.et);
-    const uint32_t c = SR ? nv_code_sr(x_n, sb, inv, t.st_n, u[i]) : nv_code_rne(x_n, sb, inv, t.st_n);
-    out[i >> 3] |= c << (4 * (i & 7));
+  if constexpr (SR) {
+    out[0] = nv_codes8_sr(v, u, t, k);
+    out[1] = nv_codes8_sr(v + 8, u + 8, t, k);
+  } else {
+    out[0] = nv_codes8_rne(v, t, k);
+    out[1] = nv_codes8_rne(v + 8, t, k);
   }
   return k;
 }
@@ -196,14 +200,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
     if (col >= c0 + nc) continue;
     const int64_t grow0 = p.row0 + r0 + h * 32;  // first row of the group in the whole tensor
     uint32_t u[32];
-    if constexpr (SR) {
-      const uint64_t n0 = p.sr_offset + (uint64_t)(col * p.total_rows + grow0);
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const u32x4 w = philox_words4(n0 + i, p.sr_seed);
-        u[i] = w.x; u[i + 1] = w.y; u[i + 2] = w.z; u[i + 3] = w.w;
-      }
-    }
+    if constexpr (SR) philox_words<32>(p.sr_offset + (uint64_t)(col * p.total_rows + grow0), p.sr_seed, u);
     uint8_t* cdst = p.codes_col + col * p.ld_col_codes + grow0 / 2;
     uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
     if constexpr (FMT == kMX) {
