@@ -44,13 +44,41 @@ __device__ __forceinline__ void to_f32(const Raw<float>& r, float v[8]) {
   v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
 }
 
-// y = (1/4) H16 (s * x) over the 16 elements held by a lane pair (this lane holds
-// positions half*8 .. half*8+7). Stages h = 1, 2, 4 inside the lane, h = 8 across
-// the pair; fp32 throughout, then the exact scaling by 1/4.
-__device__ __forceinline__ void rht16_pair(float v[8], uint32_t half, uint32_t sign_mask) {
-  const uint32_t bits = sign_mask >> (half * 8);
+// Sign flips of the Hadamard transform applied to raw inputs. For bf16 a lane's
+// 8 values are 4 dwords, so the flips are 4 XOR masks precomputed per lane.
+struct SignFlips {
+  uint32_t d[4];  // bf16: per dword; fp32: bits 0..7 of d[0] hold the 8 flags
+};
+
+template <typename T>
+__device__ __forceinline__ SignFlips make_flips(uint32_t sign_mask, uint32_t half) {
+  SignFlips f;
+  const uint32_t bits = (sign_mask >> (half * 8)) & 0xFFu;
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = as_f(as_u(v[i]) ^ (((bits >> i) & 1u) << 31));
+    for (int k = 0; k < 4; ++k)
+      f.d[k] = (((bits >> (2 * k)) & 1u) << 15) | (((bits >> (2 * k + 1)) & 1u) << 31);
+  } else {
+    f.d[0] = bits;
+    f.d[1] = f.d[2] = f.d[3] = 0;
+  }
+  return f;
+}
+
+__device__ __forceinline__ void flip(Raw<uint16_t>& r, const SignFlips& f) {
+  r.w.x ^= f.d[0]; r.w.y ^= f.d[1]; r.w.z ^= f.d[2]; r.w.w ^= f.d[3];
+}
+__device__ __forceinline__ void flip(Raw<float>& r, const SignFlips& f) {
+  float* p = reinterpret_cast<float*>(&r);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = as_f(as_u(p[i]) ^ (((f.d[0] >> i) & 1u) << 31));
+}
+
+// z = H16 (s * x) over the 16 elements held by a lane pair (this lane holds
+// positions half*8 .. half*8+7; the signs are already applied). Stages h = 1, 2, 4
+// inside the lane, h = 8 across the pair; fp32. The transform's factor 1/4 is
+// left to the caller (an exact power of two, folded into the block scale).
+__device__ __forceinline__ void h16_pair(float v[8], uint32_t half) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -62,33 +90,48 @@ __device__ __forceinline__ void rht16_pair(float v[8], uint32_t half, uint32_t s
       }
     }
   }
+  // stage 8: lane 2j (holding a) keeps a + b, lane 2j+1 (holding b) keeps a + (-b)
+  const uint32_t neg = half << 31;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float o = dppf<kQuadSwap1>(v[i]);
-    v[i] = half ? (o - v[i]) : (v[i] + o);
+    v[i] = o + as_f(as_u(v[i]) ^ neg);
   }
+}
+
+// NaN-propagating max of |v| over 8 values (v_maximum3_f32 with abs modifiers).
+__device__ __forceinline__ float absmax8(const float* v) {
+  float m = __builtin_elementwise_maximum(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] *= 0.25f;
+  for (int i = 2; i < 8; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
+  return m;
 }
 
 __device__ __forceinline__ void sr_words8(uint64_t n, uint64_t seed, uint32_t u[8]) {
   philox_words<8>(n, seed, u);
 }
 
+// E8M0 byte of a block from its amax bits (exponent field ea of max|z|), where the
+// values z are the real values times 2^kShift (kShift = 2 when the Hadamard
+// transform's 1/4 is still to be applied). 255: NaN or Inf in the block.
+template <int kShift>
+__device__ __forceinline__ uint32_t mx_byte(uint32_t amax_bits) {
+  const uint32_t ea = (amax_bits & 0x7FFFFFFFu) >> 23;
+  return ea >= 255u ? 255u : (ea > 2u + kShift ? ea - 2u - kShift : 0u);
+}
+
 // MXFP4: 8 values of one lane (a quarter of a 32-block) -> 8 codes, block byte.
-template <bool SR>
+template <bool SR, int kShift>
 __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t u[8],
                                                uint32_t& byte) {
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
-  am = max(am, dpp<kQuadSwap1>(am));
-  am = max(am, dpp<kQuadSwap2>(am));
-  const uint32_t ea = am >> 23;  // 255: NaN or Inf in the block
-  byte = ea >= 255u ? 255u : (ea > 2u ? ea - 2u : 0u);
+  float am = absmax8(v);
+  am = __builtin_elementwise_maximum(am, dppf<kQuadSwap1>(am));
+  am = __builtin_elementwise_maximum(am, dppf<kQuadSwap2>(am));
+  byte = mx_byte<kShift>(as_u(am));
+  const uint32_t b = min(byte, 252u);
   uint32_t packed = 0;
   if constexpr (SR) {
-    const float inv = as_f((254u - min(byte, 252u)) << 23);  // 2^-E
+    const float inv = as_f((254u - b - kShift) << 23);  // 2^-(E + kShift), exact
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float y = fabsf(v[i]) * inv;
@@ -96,7 +139,7 @@ __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t 
       packed |= c << (4 * i);
     }
   } else {
-    packed = fp4x8_from_f32(v, e8m0_operand(min(byte, 254u)));
+    packed = fp4x8_from_f32(v, e8m0_operand(b + kShift));
   }
   return byte == 255u ? 0u : packed;
 }
@@ -120,27 +163,21 @@ __device__ __forceinline__ uint32_t mx_encode8_bf16(const uint4& r, uint32_t& by
 template <bool SR>
 __device__ __forceinline__ uint32_t nv_encode8(const float v[8], const uint32_t u[8],
                                                const NvTensor& t, uint32_t& byte) {
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
-  am = max(am, dpp<kQuadSwap1>(am));
-  uint32_t signs = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) signs |= (as_u(v[i]) >> 31) << (4 * i + 3);
-  if (t.mode == 2 || am >= 0x7F800000u) {
-    byte = 0x7Fu;
-    return 0u;
+  float am = absmax8(v);
+  am = __builtin_elementwise_maximum(am, dppf<kQuadSwap1>(am));
+  if (t.mode != 0) {  // uniform: s_t NaN, or s_t == 0 (sign-only codes)
+    byte = t.mode == 2 ? 0x7Fu : 0u;
+    return t.mode == 2 ? 0u : fp4x8_from_f32(v, 0.0f) & 0x88888888u;
   }
-  if (t.mode == 1) {
-    byte = 0u;
-    return signs;
-  }
-  const float a_n = ldexpf(as_f(am), -t.et);
-  const uint32_t k = nv_block_scale(a_n, t.st_n);
-  byte = k;
-  if (k == 0u) return signs;
-  if constexpr (SR) return nv_codes8_sr(v, u, t, k);
-  return nv_codes8_rne(v, t, k);
+  const uint32_t amb = as_u(am) & 0x7FFFFFFFu;
+  const bool nanb = amb >= 0x7F800000u;
+  const uint32_t k = nv_block_scale(ldexpf(as_f(nanb ? 0u : amb), -t.et), t.st_n);
+  uint32_t packed;
+  if constexpr (SR) packed = nv_codes8_sr(v, u, t, max(k, 1u));
+  else packed = nv_codes8_rne(v, t, max(k, 1u));
+  if (k == 0u) packed &= 0x88888888u;  // the block scale underflowed: sign bits only
+  byte = nanb ? 0x7Fu : k;
+  return nanb ? 0u : packed;
 }
 
 }  // namespace mxq

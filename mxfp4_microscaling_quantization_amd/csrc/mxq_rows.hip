@@ -51,6 +51,9 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
     nt = nv_tensor(*p.amax);
     if (p.tensor_scale && blockIdx.x == 0 && threadIdx.x == 0) *p.tensor_scale = nt.st;
   }
+  // a chunk's parity (its half of a 16-element Hadamard chunk) is the lane's parity
+  SignFlips flips;
+  if constexpr (RHT) flips = make_flips<T>(p.sign_mask, threadIdx.x & 1u);
   Raw<T> raw[kUnroll];
 #pragma unroll
   for (int j = 0; j < kUnroll; ++j) {
@@ -66,12 +69,13 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
     if constexpr (FMT == kMX && !SR && !RHT && sizeof(T) == 2) {
       packed = mx_encode8_bf16(raw[j].w, byte);
     } else {
+      if constexpr (RHT) flip(raw[j], flips);
       float v[8];
       to_f32(raw[j], v);
-      if constexpr (RHT) rht16_pair(v, c & 1u, p.sign_mask);
+      if constexpr (RHT) h16_pair(v, threadIdx.x & 1u);
       uint32_t u[8];
       if constexpr (SR) sr_words8(p.sr_base + (uint64_t)c * 8, p.sr_seed, u);
-      if constexpr (FMT == kMX) packed = mx_encode8<SR>(v, u, byte);
+      if constexpr (FMT == kMX) packed = mx_encode8<SR, RHT ? 2 : 0>(v, u, byte);
       else packed = nv_encode8<SR>(v, u, nt, byte);
     }
     if (c < p.chunks) {
@@ -290,22 +294,30 @@ __global__ void amax_init_kernel(float* out) { *reinterpret_cast<uint32_t*>(out)
 template <typename T, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void amax_kernel(RowParams p, uint32_t* out) {
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  // m: the largest |x| bit pattern (NaN > Inf > finite), as fp32 bits
   uint32_t m = 0;
+  constexpr int U = 8;
   const uint32_t stride = gridDim.x * kThreads;
-  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < p.chunks; c0 += stride * kUnroll) {
-    Raw<T> r[kUnroll];
+  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < p.chunks; c0 += stride * U) {
+    Raw<T> r[U];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
+    for (int j = 0; j < U; ++j) {
       const uint32_t c = c0 + j * stride;
       if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), r[j]);
       else zero_raw(r[j]);
     }
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      float v[8];
-      to_f32(r[j], v);
+    for (int j = 0; j < U; ++j) {
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w[4] = {r[j].w.x, r[j].w.y, r[j].w.z, r[j].w.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, as_u(v[i]) & 0x7FFFFFFFu);
+        for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu) << 16);
+      } else {
+        float v[8];
+        to_f32(r[j], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = max(m, as_u(v[i]) & 0x7FFFFFFFu);
+      }
     }
   }
 #pragma unroll
@@ -336,8 +348,10 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
     p.chunks = (uint32_t)(nr * cpr);
     FastDivHost fd = make_fastdiv((uint32_t)cpr);
     p.cpr = FastDiv{fd.d, fd.m, fd.s};
-    const uint32_t want = (p.chunks + kThreads * 4 * kUnroll - 1) / (kThreads * 4 * kUnroll);
-    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 4096));
+    // few workgroups: each ends with one atomic on the same word, and contention on
+    // that word costs more than the shorter grid-stride loops save
+    const uint32_t want = (p.chunks + kThreads * 8 - 1) / (kThreads * 8);
+    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 512));
     uint32_t* out = reinterpret_cast<uint32_t*>(amax_out);
     const bool contig = ldx == cols;
     if (dtype == 0) {
@@ -360,15 +374,19 @@ template <typename T, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void rht_apply_kernel(RowParams p, float* y) {
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
+  const SignFlips flips = make_flips<T>(p.sign_mask, threadIdx.x & 1u);
 #pragma unroll
   for (int j = 0; j < kUnroll; ++j) {
     const uint32_t c = base + j * kThreads;
     Raw<T> r;
     if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), r);
     else zero_raw(r);
+    flip(r, flips);
     float v[8];
     to_f32(r, v);
-    rht16_pair(v, c & 1u, p.sign_mask);
+    h16_pair(v, threadIdx.x & 1u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= 0.25f;
     if (c < p.chunks) {
       float4* o = reinterpret_cast<float4*>(y) + (size_t)c * 2;
       o[0] = make_float4(v[0], v[1], v[2], v[3]);

@@ -36,10 +36,9 @@ struct TileParams {
   float* tensor_scale;
 };
 
-// In-thread Hadamard of 16 values (stages 1, 2, 4, 8, then 1/4); signs by position.
-__device__ __forceinline__ void rht16_local(float* v, uint32_t sign_mask) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = as_f(as_u(v[i]) ^ (((sign_mask >> i) & 1u) << 31));
+// In-thread Hadamard of 16 values (signs already applied): stages 1, 2, 4, 8 in
+// fp32; the factor 1/4 is folded into the block scale by the caller.
+__device__ __forceinline__ void h16_local(float* v) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -51,20 +50,23 @@ __device__ __forceinline__ void rht16_local(float* v, uint32_t sign_mask) {
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
 }
 
-// MXFP4 encode of 32 values held by one thread; codes into 4 dwords.
-template <bool SR>
-__device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* u, uint32_t out[4]) {
-  uint32_t am = 0;
+__device__ __forceinline__ float absmax32(const float* v) {
+  float m = __builtin_elementwise_maximum(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
 #pragma unroll
-  for (int i = 0; i < 32; ++i) am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
-  const uint32_t ea = am >> 23;
-  const uint32_t byte = ea >= 255u ? 255u : (ea > 2u ? ea - 2u : 0u);
+  for (int i = 2; i < 32; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
+  return m;
+}
+
+// MXFP4 encode of 32 values held by one thread (real values times 2^kShift);
+// codes into 4 dwords, returns the block byte.
+template <bool SR, int kShift>
+__device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* u, uint32_t out[4]) {
+  const uint32_t byte = mx_byte<kShift>(as_u(absmax32(v)));
+  const uint32_t b = min(byte, 252u);
   if constexpr (SR) {
-    const float inv = as_f((254u - min(byte, 252u)) << 23);
+    const float inv = as_f((254u - b - kShift) << 23);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       uint32_t packed = 0;
@@ -78,7 +80,7 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* 
       out[d] = byte == 255u ? 0u : packed;
     }
   } else {
-    const float scale = e8m0_operand(min(byte, 254u));
+    const float scale = e8m0_operand(b + kShift);
 #pragma unroll
     for (int d = 0; d < 4; ++d) out[d] = byte == 255u ? 0u : fp4x8_from_f32(v + 8 * d, scale);
   }
@@ -89,31 +91,28 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* 
 template <bool SR>
 __device__ __forceinline__ uint32_t nv_encode16(const float* v, const uint32_t* u, const NvTensor& t,
                                                 uint32_t out[2]) {
-  uint32_t am = 0;
-  uint32_t signs[2] = {0, 0};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
-    signs[i >> 3] |= (as_u(v[i]) >> 31) << (4 * (i & 7) + 3);
+  if (t.mode != 0) {
+    out[0] = t.mode == 2 ? 0u : fp4x8_from_f32(v, 0.0f) & 0x88888888u;
+    out[1] = t.mode == 2 ? 0u : fp4x8_from_f32(v + 8, 0.0f) & 0x88888888u;
+    return t.mode == 2 ? 0x7Fu : 0u;
   }
-  if (t.mode == 2 || am >= 0x7F800000u) {
-    out[0] = out[1] = 0u;
-    return 0x7Fu;
-  }
-  out[0] = signs[0];
-  out[1] = signs[1];
-  if (t.mode == 1) return 0u;
-  const float a_n = ldexpf(as_f(am), -t.et);
-  const uint32_t k = nv_block_scale(a_n, t.st_n);
-  if (k == 0u) return 0u;
+  const float am = __builtin_elementwise_maximum(absmax8(v), absmax8(v + 8));
+  const uint32_t amb = as_u(am) & 0x7FFFFFFFu;
+  const bool nanb = amb >= 0x7F800000u;
+  const uint32_t k = nv_block_scale(ldexpf(as_f(nanb ? 0u : amb), -t.et), t.st_n);
   if constexpr (SR) {
-    out[0] = nv_codes8_sr(v, u, t, k);
-    out[1] = nv_codes8_sr(v + 8, u + 8, t, k);
+    out[0] = nv_codes8_sr(v, u, t, max(k, 1u));
+    out[1] = nv_codes8_sr(v + 8, u + 8, t, max(k, 1u));
   } else {
-    out[0] = nv_codes8_rne(v, t, k);
-    out[1] = nv_codes8_rne(v + 8, t, k);
+    out[0] = nv_codes8_rne(v, t, max(k, 1u));
+    out[1] = nv_codes8_rne(v + 8, t, max(k, 1u));
   }
-  return k;
+  if (k == 0u) {
+    out[0] &= 0x88888888u;
+    out[1] &= 0x88888888u;
+  }
+  if (nanb) out[0] = out[1] = 0u;
+  return nanb ? 0x7Fu : k;
 }
 
 template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
@@ -132,6 +131,9 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
     if (p.tensor_scale && blockIdx.x == 0 && t == 0) *p.tensor_scale = nt.st;
   }
 
+  SignFlips flips;
+  if constexpr (RHT && ROW) flips = make_flips<T>(p.sign_mask, t & 1u);
+
   // ---- phase 1: load (+ row-wise quantise), park raw values in LDS
   constexpr int kChunks = kTileR * kTileC / 8 / kTileThreads;  // 8 per thread
   Raw<T> raw[kChunks];
@@ -148,15 +150,17 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
     const int row = (int)(q >> 4), cc = (int)(q & 15u);
     *reinterpret_cast<Raw<T>*>(&tile[row][cc * 8]) = raw[j];
     if constexpr (ROW) {
+      Raw<T> rr = raw[j];
+      if constexpr (RHT) flip(rr, flips);
       float v[8];
-      to_f32(raw[j], v);
-      if constexpr (RHT) rht16_pair(v, cc & 1, p.sign_mask);
+      to_f32(rr, v);
+      if constexpr (RHT) h16_pair(v, t & 1u);
       uint32_t u[8];
       const int64_t grow = p.row0 + r0 + row;
       const int64_t col = c0 + cc * 8;
       if constexpr (SR) sr_words8(p.sr_offset + (uint64_t)(grow * p.cols + col), p.sr_seed, u);
       uint32_t byte, packed;
-      if constexpr (FMT == kMX) packed = mx_encode8<SR>(v, u, byte);
+      if constexpr (FMT == kMX) packed = mx_encode8<SR, RHT ? 2 : 0>(v, u, byte);
       else packed = nv_encode8<SR>(v, u, nt, byte);
       if (row < nr && cc * 8 < nc) {
         const int64_t lr = r0 + row;  // row within the slab
@@ -175,21 +179,23 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   float v0[32], v1[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
+    // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
+    const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) : 0u;
     if constexpr (sizeof(T) == 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][cp * 2]);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][cp * 2]) ^ (s ? 0x80008000u : 0u);
       v0[i] = as_f(w << 16);
       v1[i] = as_f(w & 0xFFFF0000u);
     } else {
       const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][cp * 2]);
-      v0[i] = w.x;
-      v1[i] = w.y;
+      v0[i] = as_f(as_u(w.x) ^ (s << 31));
+      v1[i] = as_f(as_u(w.y) ^ (s << 31));
     }
   }
   if constexpr (RHT) {
-    rht16_local(v0, p.sign_mask);
-    rht16_local(v0 + 16, p.sign_mask);
-    rht16_local(v1, p.sign_mask);
-    rht16_local(v1 + 16, p.sign_mask);
+    h16_local(v0);
+    h16_local(v0 + 16);
+    h16_local(v1);
+    h16_local(v1 + 16);
   }
   const int vrows = nr - h * 32;  // valid rows of this 32-row group
   if (vrows <= 0) return;
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
     uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
     if constexpr (FMT == kMX) {
       uint32_t out[4];
-      const uint32_t byte = mx_encode32<SR>(v, u, out);
+      const uint32_t byte = mx_encode32<SR, RHT ? 2 : 0>(v, u, out);
       *reinterpret_cast<uint4*>(cdst) = make_uint4(out[0], out[1], out[2], out[3]);
       sdst[grow0 / 32] = (uint8_t)byte;
     } else {
