@@ -132,12 +132,11 @@ __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t 
   uint32_t packed = 0;
   if constexpr (SR) {
     const float inv = as_f((254u - b - kShift) << 23);  // 2^-(E + kShift), exact
+    float q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float y = fabsf(v[i]) * inv;
-      const uint32_t c = e2m1_sr(y, u[i]) | ((as_u(v[i]) >> 31) << 3);
-      packed |= c << (4 * i);
-    }
+    for (int i = 0; i < 8; ++i)
+      q[i] = as_f(as_u(e2m1_sr_value(fabsf(v[i]) * inv, u[i])) | (as_u(v[i]) & 0x80000000u));
+    packed = fp4x8_from_f32(q, 1.0f);
   } else {
     packed = fp4x8_from_f32(v, e8m0_operand(b + kShift));
   }
@@ -171,7 +170,7 @@ __device__ __forceinline__ uint32_t nv_encode8(const float v[8], const uint32_t 
   }
   const uint32_t amb = as_u(am) & 0x7FFFFFFFu;
   const bool nanb = amb >= 0x7F800000u;
-  const uint32_t k = nv_block_scale(ldexpf(as_f(nanb ? 0u : amb), -t.et), t.st_n);
+  const uint32_t k = nv_block_scale_fast(ldexpf(as_f(nanb ? 0u : amb), -t.et), t.st_n);
   uint32_t packed;
   if constexpr (SR) packed = nv_codes8_sr(v, u, t, max(k, 1u));
   else packed = nv_codes8_rne(v, t, max(k, 1u));

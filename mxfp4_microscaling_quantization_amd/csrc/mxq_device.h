@@ -190,17 +190,34 @@ __device__ __forceinline__ uint32_t philox_word(uint64_t n, uint64_t seed) {
   return s == 0 ? w.x : (s == 1 ? w.y : (s == 2 ? w.z : w.w));
 }
 
+// The E2M1 grid value at or below y >= 0 (as fp32) and the gap to the next one,
+// from the bits of y: for y >= 1 the grid keeps one mantissa bit, on [0.5, 1) it
+// is 0.5, below 0.5 it is 0. The gap is 2^(max(e, 0) - 1) for y in [2^e, 2^(e+1)).
+__device__ __forceinline__ void e2m1_floor_step(float y, float& lo, float& step) {
+  const uint32_t b = as_u(y);
+  const uint32_t e = b >> 23;  // biased exponent (y >= 0)
+  const uint32_t mask = e >= 127u ? 0xFFC00000u : (e == 126u ? 0xFF800000u : 0u);
+  lo = as_f(b & mask);
+  step = as_f((max(e, 127u) - 1u) << 23);
+}
+
+// (r + 1/2) / 2^16 with r the top 16 bits of the random word u (17 significant bits).
+__device__ __forceinline__ float sr_offset16(uint32_t u) {
+  return (float)((u >> 15) | 1u) * (1.0f / 131072.0f);
+}
+
 // Stochastic E2M1 rounding of an exact fp32 magnitude y with random word u:
 // up iff y > lo + step * (r + 1/2) / 2^16, r = u >> 16; y >= 6 gives 6.
 // lo + step * (r + 1/2) / 2^16 has at most 20 significant bits: exact in fp32.
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
-  const uint32_t lo = e2m1_floor(y);
-  const float vlo = e2m1_value(lo);
-  const float step = e2m1_value(lo + 1u) - vlo;
-  const float thr = vlo + step * ((float)(u >> 16) + 0.5f) * (1.0f / 65536.0f);
-  const uint32_t c = (y > thr) ? lo + 1u : lo;
-  return lo >= 7u ? 7u : c;
+// Returns the rounded grid value (<= 6) as fp32; the caller converts it (exactly).
+__device__ __forceinline__ float e2m1_sr_value(float y, uint32_t u) {
+  float lo, step;
+  e2m1_floor_step(y, lo, step);
+  const float thr = fmaf(step, sr_offset16(u), lo);  // exact: at most 20 significant bits
+  return fminf(y > thr ? lo + step : lo, 6.0f);
 }
+
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) { return e2m1_rne(e2m1_sr_value(y, u)); }
 
 // ---------------------------------------------------------------------------
 // Unsigned division of i < 2^30 by an invariant d >= 1: q = (i * m) >> s with
@@ -325,72 +342,100 @@ __device__ __forceinline__ uint32_t nv_code_sr(float x_n, float sb, float inv, f
   return fmaf(thr * sb, st_n, -x_n) < 0.0f ? lo + 1u : lo;
 }
 
-// Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1.
-// Nearest even: the quotient is approximated in fp32 and rounded by the hardware
-// conversion; values that land within 64 ulp of a value with 3 significant bits
-// (every rounding midpoint is one) are decided again exactly. When s_t >= 2^-80
-// the exact tests use s_t itself (no product underflows), else normalised values.
-__device__ __forceinline__ uint32_t nv_codes8_rne(const float* v, const NvTensor& t, uint32_t k) {
-  const float sb = e4m3_value(k);
-  const float r = __builtin_amdgcn_rcpf(sb * t.st_n);
-  uint32_t packed = 0;
-  if (t.et >= -80) {
-    const float inv = ldexpf(r, -t.et);
-    float y[8];
-    uint32_t flag = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      y[i] = v[i] * inv;
-      flag |= (uint32_t)near_3bit(fabsf(y[i])) << i;
-    }
-    packed = fp4x8_from_f32(y, 1.0f);
-    if (flag) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if ((flag >> i) & 1u) {
-          const uint32_t c = nv_code_exact(fabsf(v[i]), sb, t.st) | ((as_u(v[i]) >> 31) << 3);
-          packed = (packed & ~(0xFu << (4 * i))) | (c << (4 * i));
-        }
-      }
-    }
-    return packed;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x_n = ldexpf(fabsf(v[i]), -t.et);
-    const uint32_t c = nv_code_rne(x_n, sb, r, t.st_n) | ((as_u(v[i]) >> 31) << 3);
-    packed |= c << (4 * i);
-  }
-  return packed;
-}
-
 // Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1,
-// stochastic rounding with words u.
-__device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t* u, const NvTensor& t,
-                                                 uint32_t k) {
+// nearest even. The quotient y = |x| / (s_b s_t) is approximated in fp32 to a few
+// ulp and rounded twice by the hardware conversion, at y (1 - 2^-20) and
+// y (1 + 2^-20). Equal codes bracket the exact quotient and are the answer; where
+// they differ a single rounding midpoint m lies between them, and the sign of
+// fma(m s_b, s_t, -|x|) (exact) picks the lower code, the upper one, or on an
+// exact tie the even one. When s_t < 2^-80 the same tests run on values
+// normalised by 2^-et.
+__device__ __forceinline__ uint32_t nv_codes8_rne(const float* v, const NvTensor& t, uint32_t k) {
   const float sb = e4m3_value(k);
   const float r = __builtin_amdgcn_rcpf(sb * t.st_n);
   const bool fast = t.et >= -80;
   const float inv = fast ? ldexpf(r, -t.et) : r;
   const float sts = fast ? t.st : t.st_n;
-  uint32_t packed = 0;
+  float ylo[8], yhi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float ax = fabsf(v[i]);
-    const float xs = fast ? ax : ldexpf(ax, -t.et);
+    const float xs = fast ? v[i] : ldexpf(v[i], -t.et);
     const float y = xs * inv;
-    uint32_t lo = e2m1_floor(y);
-    if (near_3bit(y)) lo = nv_floor_exact(xs, sb, sts);
-    uint32_t c = 7u;
-    if (lo < 7u) {
-      const float vlo = e2m1_value(lo);
-      const float step = e2m1_value(lo + 1u) - vlo;
-      const float thr = vlo + step * ((float)(u[i] >> 16) + 0.5f) * (1.0f / 65536.0f);
-      c = fmaf(thr * sb, sts, -xs) < 0.0f ? lo + 1u : lo;
-    }
-    packed |= (c | ((as_u(v[i]) >> 31) << 3)) << (4 * i);
+    ylo[i] = y * 0.99999905f;  // 1 - 2^-20
+    yhi[i] = y * 1.00000095f;  // 1 + 2^-20
   }
-  return packed;
+  const uint32_t clo = fp4x8_from_f32(ylo, 1.0f);
+  const uint32_t chi = fp4x8_from_f32(yhi, 1.0f);
+  const uint32_t diff = clo ^ chi;
+  if (diff == 0u) return clo;
+  // some element lies within 2^-20 of a midpoint: decide exactly the ones that do
+  uint32_t out = clo;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if ((diff >> (4 * i)) & 0xFu) {
+      const uint32_t lo = (clo >> (4 * i)) & 0xFu, hi = (chi >> (4 * i)) & 0xFu;
+      // the two neighbouring grid values, decoded together: m is their midpoint
+      const f32x2_t g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((lo & 7u) | ((hi & 7u) << 4), 1.0f, 0);
+      const float m = 0.5f * (g.x + g.y);
+      const float xs = fast ? fabsf(v[i]) : ldexpf(fabsf(v[i]), -t.et);
+      const float d = fmaf(m * sb, sts, -xs);  // > 0: the quotient is below m
+      const uint32_t c = d > 0.0f ? lo : (d < 0.0f ? hi : ((lo & 1u) ? hi : lo));
+      out = (out & ~(0xFu << (4 * i))) | (c << (4 * i));
+    }
+  }
+  return out;
+}
+
+// Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1,
+// stochastic rounding with words u. With lo and step taken from an approximate
+// quotient, the decision |x| > (lo + step (r + 1/2) 2^-16) s_b s_t is exact (one
+// FMA; the coefficient has at most 23 significant bits). An approximate lo can
+// only be wrong within a few ulp of a grid value, where both candidate decisions
+// return that same grid value, so no correction is needed.
+__device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t* u, const NvTensor& t,
+                                                 uint32_t k) {
+  const float sb = e4m3_value(k);
+  const float r = __builtin_amdgcn_rcpf(sb * t.st_n);
+  float q[8];
+  if (t.et >= -80) {
+    const float inv = ldexpf(r, -t.et);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float ax = fabsf(v[i]);
+      const float y = ax * inv;
+      float lo, step;
+      e2m1_floor_step(y, lo, step);
+      const float c = fmaf(step * sb, sr_offset16(u[i]), lo * sb);
+      const bool up = fmaf(c, t.st, -ax) < 0.0f;
+      q[i] = as_f(as_u(fminf(up ? lo + step : lo, 6.0f)) | (as_u(v[i]) & 0x80000000u));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xs = ldexpf(fabsf(v[i]), -t.et);
+      const float y = xs * r;
+      float lo, step;
+      e2m1_floor_step(y, lo, step);
+      const float c = fmaf(step * sb, sr_offset16(u[i]), lo * sb);
+      const bool up = fmaf(c, t.st_n, -xs) < 0.0f;
+      q[i] = as_f(as_u(fminf(up ? lo + step : lo, 6.0f)) | (as_u(v[i]) & 0x80000000u));
+    }
+  }
+  return fp4x8_from_f32(q, 1.0f);  // grid values: the conversion is exact
+}
+
+// E4M3 code of the block scale, nearest even of the exact quotient a_n / (6 st_n):
+// the approximate quotient is converted twice, at q (1 -+ 2^-20); equal codes are
+// the answer, else the exact test against the midpoint between them decides.
+__device__ __forceinline__ uint32_t nv_block_scale_fast(float a_n, float st_n) {
+  const float q = a_n * __builtin_amdgcn_rcpf(6.0f * st_n);
+  const float qlo = fminf(q * 0.99999905f, 448.0f), qhi = fminf(q * 1.00000095f, 448.0f);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qlo, qhi, 0, false);
+  const uint32_t klo = w & 0x7Fu, khi = (w >> 8) & 0x7Fu;
+  if (klo == khi) return klo;
+  const float mu6 = 3.0f * (e4m3_value(klo) + e4m3_value(khi));  // 6 * midpoint, exact
+  const float d = fmaf(mu6, st_n, -a_n);
+  return d > 0.0f ? klo : (d < 0.0f ? khi : ((klo & 1u) ? khi : klo));
 }
 
 }  // namespace mxq

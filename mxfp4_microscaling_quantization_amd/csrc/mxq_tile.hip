@@ -4,12 +4,12 @@
 // 16-byte chunks (a wave reads four 256-byte row segments per instruction),
 // quantises them row-wise if asked (blocks along the row span a DPP quad, exactly
 // as in the row kernel) and parks the raw values in LDS. Phase 2: thread t owns
-// the column pair 2*(t%64), 2*(t%64)+1 over rows 32*(t/64) .. +31 and reads them as
-// one dword (bf16) per row: a wave's 64 lanes read 64 consecutive dwords of one
-// LDS row, so the column walk is free of bank conflicts without padding. The
-// optional Hadamard transform runs along the rows in registers, each column's 32
-// codes leave as one 16-byte store, and the four row groups of a column land in
-// one contiguous 64-byte run written by the same workgroup.
+// the column pair 2*(t/4), 2*(t/4)+1 over rows 32*(t%4) .. +31 and reads them as
+// one dword (bf16) per row. The LDS tile is XOR-swizzled so that these reads hit
+// all 32 banks. The optional Hadamard transform runs along the rows in registers,
+// each column's 32 codes leave as one 16-byte store, and the four lanes of a
+// column pair sit side by side, so each store instruction writes 64 contiguous
+// bytes per column.
 #include <algorithm>
 
 #include "mxq_blocks.h"
@@ -69,15 +69,13 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* 
     const float inv = as_f((254u - b - kShift) << 23);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      uint32_t packed = 0;
+      float q[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = d * 8 + i;
-        const float y = fabsf(v[e]) * inv;
-        const uint32_t c = e2m1_sr(y, u[e]) | ((as_u(v[e]) >> 31) << 3);
-        packed |= c << (4 * i);
+        q[i] = as_f(as_u(e2m1_sr_value(fabsf(v[e]) * inv, u[e])) | (as_u(v[e]) & 0x80000000u));
       }
-      out[d] = byte == 255u ? 0u : packed;
+      out[d] = byte == 255u ? 0u : fp4x8_from_f32(q, 1.0f);
     }
   } else {
     const float scale = e8m0_operand(b + kShift);
@@ -99,7 +97,7 @@ __device__ __forceinline__ uint32_t nv_encode16(const float* v, const uint32_t* 
   const float am = __builtin_elementwise_maximum(absmax8(v), absmax8(v + 8));
   const uint32_t amb = as_u(am) & 0x7FFFFFFFu;
   const bool nanb = amb >= 0x7F800000u;
-  const uint32_t k = nv_block_scale(ldexpf(as_f(nanb ? 0u : amb), -t.et), t.st_n);
+  const uint32_t k = nv_block_scale_fast(ldexpf(as_f(nanb ? 0u : amb), -t.et), t.st_n);
   if constexpr (SR) {
     out[0] = nv_codes8_sr(v, u, t, max(k, 1u));
     out[1] = nv_codes8_sr(v + 8, u + 8, t, max(k, 1u));
@@ -114,6 +112,12 @@ __device__ __forceinline__ uint32_t nv_encode16(const float* v, const uint32_t* 
   if (nanb) out[0] = out[1] = 0u;
   return nanb ? 0x7Fu : k;
 }
+
+// LDS column index of element column c in tile row r. Phase 2 reads, at one
+// instant, column pairs 16a .. 16a+15 in rows 32h + i for h = 0..3; XOR-ing the
+// column-pair index with 8h (bits 3-4) spreads those 64 lanes over all 32 banks.
+// Groups of four column pairs (one 16-byte chunk of bf16) stay contiguous.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 5) & 3) << 4); }
 
 template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
 __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams p) {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   for (int j = 0; j < kChunks; ++j) {
     const uint32_t q = t + j * kTileThreads;
     const int row = (int)(q >> 4), cc = (int)(q & 15u);
-    *reinterpret_cast<Raw<T>*>(&tile[row][cc * 8]) = raw[j];
+    *reinterpret_cast<Raw<T>*>(&tile[row][swz(row, cc * 8)]) = raw[j];
     if constexpr (ROW) {
       Raw<T> rr = raw[j];
       if constexpr (RHT) flip(rr, flips);
@@ -173,20 +177,23 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   if constexpr (!COL) return;
   __syncthreads();
 
-  // ---- phase 2: column pairs over 32 rows
-  const int cp = (int)(t & 63u);
-  const int h = (int)(t >> 6);
+  // ---- phase 2: column pairs over 32 rows. Lanes 4j .. 4j+3 of a wave hold the
+  // four 32-row groups of one column pair, so a wave's store instruction writes 16
+  // columns x 64 contiguous bytes.
+  const int cp = (int)(t >> 2);
+  const int h = (int)(t & 3u);
   float v0[32], v1[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
     const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) : 0u;
     if constexpr (sizeof(T) == 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][cp * 2]) ^ (s ? 0x80008000u : 0u);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]) ^
+                         (s ? 0x80008000u : 0u);
       v0[i] = as_f(w << 16);
       v1[i] = as_f(w & 0xFFFF0000u);
     } else {
-      const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][cp * 2]);
+      const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]);
       v0[i] = as_f(as_u(w.x) ^ (s << 31));
       v1[i] = as_f(as_u(w.y) ^ (s << 31));
     }
