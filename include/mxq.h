@@ -23,7 +23,8 @@
  *
  * Status codes: MXQ_OK on success; MXQ_EINVAL for a NULL pointer, an enum out of
  * range or a negative size; MXQ_ESHAPE for a dimension that is not a multiple of
- * the block size (no padding is ever applied) or ldx < cols; MXQ_EALIGN for a
+ * the block size (no padding is ever applied), ldx < cols, or a tensor beyond the
+ * size limits (2^40 elements, 2^30 columns); MXQ_EALIGN for a
  * pointer or row stride that breaks the stated alignment; MXQ_EUNSUPPORTED for a
  * combination not provided; MXQ_EHIP when a launch fails. rows == 0 is a no-op
  * that returns MXQ_OK. Data-dependent conditions (NaN, Inf, zeros, extreme

@@ -11,6 +11,12 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Size limits of every entry point: at most 2^40 elements and 2^30 columns (launch
+// grids and per-launch element indices then stay within 32 bits).
+bool too_large(int64_t rows, int64_t cols) {
+  return cols > ((int64_t)1 << 30) || rows > ((int64_t)1 << 40) / cols;
+}
+
 mxq_status from_hip(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_EHIP; }
 
 // Philox4x32-10 on the host (same published definition as the device copy).
@@ -52,7 +58,7 @@ mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t col
   if (cols == 0 || ldx < cols) return MXQ_ESHAPE;
   if (row && cols % bs) return MXQ_ESHAPE;
   if (col && (rows % bs || cols % 8)) return MXQ_ESHAPE;
-  if (rows > ((int64_t)1 << 40) / cols) return MXQ_ESHAPE;  // 2^40 elements at most
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
   const int64_t esz = dt == MXQ_BF16 ? 2 : 4;
   if (!aligned(x, 16) || (ldx * esz) % 16) return MXQ_EALIGN;
   if (row && (!aligned(codes_row, 16) || !aligned(scales_row, 4))) return MXQ_EALIGN;
@@ -152,7 +158,7 @@ mxq_status mxq_dequantize(const uint8_t* codes, const uint8_t* scales, mxq_forma
   if (fmt == MXQ_NVFP4 && !tensor_scale) return MXQ_EINVAL;
   const int64_t bs = fmt == MXQ_MXFP4 ? 32 : 16;
   if (cols == 0 || cols % bs) return MXQ_ESHAPE;
-  if (rows > ((int64_t)1 << 40) / cols) return MXQ_ESHAPE;
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
   if (!aligned(codes, 16) || !aligned(y, 16)) return MXQ_EALIGN;
   return from_hip(launch_dequantize(codes, scales, fmt == MXQ_MXFP4 ? kMX : kNV, rows, cols,
                                     tensor_scale, y, out_dt, reinterpret_cast<hipStream_t>(stream)));
@@ -164,7 +170,7 @@ mxq_status mxq_fp8_to_mxfp4(const uint8_t* q8, const float* s128, int64_t rows, 
   if (rows == 0) return MXQ_OK;
   if (!q8 || !s128 || !codes || !e8m0) return MXQ_EINVAL;
   if (cols == 0 || cols % 128) return MXQ_ESHAPE;
-  if (rows > ((int64_t)1 << 40) / cols) return MXQ_ESHAPE;
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
   if (!aligned(q8, 16) || !aligned(s128, 4) || !aligned(codes, 16)) return MXQ_EALIGN;
   return from_hip(launch_fp8_to_mxfp4(q8, s128, rows, cols, codes, e8m0,
                                       reinterpret_cast<hipStream_t>(stream)));
@@ -176,7 +182,7 @@ mxq_status mxq_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* e8m0, int64_t r
   if (rows == 0) return MXQ_OK;
   if (!codes || !e8m0 || !q8 || !s128) return MXQ_EINVAL;
   if (cols == 0 || cols % 128) return MXQ_ESHAPE;
-  if (rows > ((int64_t)1 << 40) / cols) return MXQ_ESHAPE;
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
   if (!aligned(codes, 16) || !aligned(e8m0, 4) || !aligned(q8, 16) || !aligned(s128, 4))
     return MXQ_EALIGN;
   return from_hip(launch_mxfp4_to_fp8(codes, e8m0, rows, cols, q8, s128,
@@ -190,7 +196,7 @@ mxq_status mxq_rht_apply(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
   if (rows == 0) return MXQ_OK;
   if (!x || !y) return MXQ_EINVAL;
   if (cols == 0 || cols % 16 || ldx < cols) return MXQ_ESHAPE;
-  if (rows > ((int64_t)1 << 40) / cols) return MXQ_ESHAPE;
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
   const int64_t esz = dt == MXQ_BF16 ? 2 : 4;
   if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(y, 16)) return MXQ_EALIGN;
   return from_hip(launch_rht_apply(x, dt, rows, cols, ldx, sign_mask & 0xFFFFu, y,
@@ -206,7 +212,7 @@ mxq_status mxq_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int
   if (rows == 0) return from_hip(launch_amax(x, dt, 0, cols, ldx, amax_out, st));
   if (!x) return MXQ_EINVAL;
   if (cols == 0 || cols % 8 || ldx < cols) return MXQ_ESHAPE;
-  if (rows > ((int64_t)1 << 40) / cols) return MXQ_ESHAPE;
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
   const int64_t esz = dt == MXQ_BF16 ? 2 : 4;
   if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(amax_out, 4)) return MXQ_EALIGN;
   return from_hip(launch_amax(x, dt, rows, cols, ldx, amax_out, st));

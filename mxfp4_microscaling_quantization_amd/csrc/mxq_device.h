@@ -131,12 +131,17 @@ struct u32x4 {
   uint32_t x, y, z, w;
 };
 
+// a ^ b ^ c in one VALU instruction (v_bitop3_b32, truth table 0x96 = odd parity)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;  // v_mad_u64_u32
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    c = u32x4{(uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
+    c = u32x4{xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1),
               (uint32_t)p0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
@@ -206,6 +211,16 @@ __device__ __forceinline__ float sr_offset16(uint32_t u) {
   return (float)((u >> 15) | 1u) * (1.0f / 131072.0f);
 }
 
+// 1 + (r + 1/2) / 2^16, built from bits: mantissa = r << 7 | 1 << 6.
+__device__ __forceinline__ float sr_offset16_plus1(uint32_t u) {
+  return as_f(((u >> 9) & 0x007FFF80u) | 0x3F800040u);
+}
+
+// |q| with the sign bit of s (one bitfield insert).
+__device__ __forceinline__ float with_sign_of(float q, float s) {
+  return __builtin_copysignf(q, s);
+}
+
 // Stochastic E2M1 rounding of an exact fp32 magnitude y with random word u:
 // up iff y > lo + step * (r + 1/2) / 2^16, r = u >> 16; y >= 6 gives 6.
 // lo + step * (r + 1/2) / 2^16 has at most 20 significant bits: exact in fp32.
@@ -213,7 +228,8 @@ __device__ __forceinline__ float sr_offset16(uint32_t u) {
 __device__ __forceinline__ float e2m1_sr_value(float y, uint32_t u) {
   float lo, step;
   e2m1_floor_step(y, lo, step);
-  const float thr = fmaf(step, sr_offset16(u), lo);  // exact: at most 20 significant bits
+  // lo + step (r + 1/2) 2^-16, exact (at most 20 significant bits)
+  const float thr = fmaf(step, sr_offset16_plus1(u), lo - step);
   return fminf(y > thr ? lo + step : lo, 6.0f);
 }
 
@@ -405,9 +421,10 @@ __device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t*
       const float y = ax * inv;
       float lo, step;
       e2m1_floor_step(y, lo, step);
-      const float c = fmaf(step * sb, sr_offset16(u[i]), lo * sb);
+      // (lo + step (r + 1/2) 2^-16) s_b, exact: written as fma(step s_b, 1 + off, (lo - step) s_b)
+      const float c = fmaf(step * sb, sr_offset16_plus1(u[i]), (lo - step) * sb);
       const bool up = fmaf(c, t.st, -ax) < 0.0f;
-      q[i] = as_f(as_u(fminf(up ? lo + step : lo, 6.0f)) | (as_u(v[i]) & 0x80000000u));
+      q[i] = with_sign_of(fminf(up ? lo + step : lo, 6.0f), v[i]);
     }
   } else {
 #pragma unroll

@@ -231,15 +231,47 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
       const uint32_t byte = sb[j];
       const bool nan = (byte & 0x7Fu) == 0x7Fu || !(fabsf(st) <= 3.40282347e38f);
       const float sbv = as_f(as_u(e4m3_value(byte & 0x7Fu)) | ((byte & 0x80u) << 24));
+      // signed E2M1 values, exact
+      float a[8];
+      const f32x2_t d[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 2),
+                            __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 3)};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t code = (w[j] >> (4 * i)) & 0xFu;
-        const float a = as_f(as_u(e2m1_value(code & 7u) * sbv) ^ ((code & 8u) << 28));
-        if (OUT_F32) {
-          out[i] = nan ? 0x7FC00000u : as_u(a * st);
-        } else {
-          out[i] = nan ? 0x7FC0u : bf16_of_product(a, st_s, k);
+      for (int h = 0; h < 4; ++h) {
+        a[2 * h] = d[h].x * sbv;  // exact: at most 6 significant bits
+        a[2 * h + 1] = d[h].y * sbv;
+      }
+      if constexpr (OUT_F32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = nan ? 0x7FC00000u : as_u(a[i] * st);
+      } else {
+        // RN_bf16(RN_f32(a s_t)) equals RN_bf16(a s_t) unless the fp32 product lands
+        // exactly on a bf16 midpoint (low half 0x8000): only such lanes take the
+        // exact residual path.
+        float pr[8];
+        bool mid = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = a[i] * st;
+          mid |= (uint16_t)as_u(pr[i]) == 0x8000u;
         }
+        uint32_t o[4];
+        if (!mid) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const bf16x2_t r = {(__bf16)pr[2 * h], (__bf16)pr[2 * h + 1]};
+            o[h] = __builtin_bit_cast(uint32_t, r);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            o[h] = bf16_of_product(a[2 * h], st_s, k) | (bf16_of_product(a[2 * h + 1], st_s, k) << 16);
+        }
+        const uint4 ov = nan ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u)
+                             : make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4*>(p.y)[c] = ov;
+        continue;
       }
     }
     if constexpr (OUT_F32) {

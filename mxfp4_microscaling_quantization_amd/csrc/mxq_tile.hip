@@ -27,7 +27,7 @@ struct TileParams {
   int64_t rows, cols;          // slab extent
   int64_t total_rows;          // whole tensor (column-wise SR index and strides)
   int64_t row0;                // slab's first row in the whole tensor
-  uint32_t tiles_c;
+  uint32_t tiles_c;            // tiles across the columns
   uint32_t sign_mask;
   uint64_t sr_seed, sr_offset;
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
@@ -121,40 +121,41 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 5) & 3) <<
 
 template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
 __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams p) {
-  // LDS tile of raw input values, row-major [128][128]
+  // LDS tile of raw input values, row-major [128][128], XOR-swizzled columns
   __shared__ T tile[kTileR][kTileC];
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t t = threadIdx.x;
-  const uint32_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x - (blockIdx.x / p.tiles_c) * p.tiles_c;
-  const int64_t r0 = (int64_t)tr * kTileR, c0 = (int64_t)tc * kTileC;
-  const int nr = (int)std::min<int64_t>(kTileR, p.rows - r0);
-  const int nc = (int)std::min<int64_t>(kTileC, p.cols - c0);
   NvTensor nt;
   if constexpr (FMT == kNV) {
     nt = nv_tensor(*p.amax);
     if (p.tensor_scale && blockIdx.x == 0 && t == 0) *p.tensor_scale = nt.st;
   }
-
   SignFlips flips;
   if constexpr (RHT && ROW) flips = make_flips<T>(p.sign_mask, t & 1u);
-
-  // ---- phase 1: load (+ row-wise quantise), park raw values in LDS
   constexpr int kChunks = kTileR * kTileC / 8 / kTileThreads;  // 8 per thread
-  Raw<T> raw[kChunks];
+
+  // tile origin and extent within the slab
+  const uint32_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x - tr * p.tiles_c;
+  const int64_t r0 = (int64_t)tr * kTileR, c0 = (int64_t)tc * kTileC;
+  const int nr = (int)std::min<int64_t>(kTileR, p.rows - r0);
+  const int nc = (int)std::min<int64_t>(kTileC, p.cols - c0);
+  Raw<T> cur[kChunks];
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     const uint32_t q = t + j * kTileThreads;
     const int row = (int)(q >> 4), cc = (int)(q & 15u);
-    if (row < nr && cc * 8 < nc) load_raw(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, raw[j]);
-    else zero_raw(raw[j]);
+    if (row < nr && cc * 8 < nc) load_raw(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, cur[j]);
+    else zero_raw(cur[j]);
   }
+
+  // ---- phase 1: row-wise quantise (optional), park raw values in LDS
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     const uint32_t q = t + j * kTileThreads;
     const int row = (int)(q >> 4), cc = (int)(q & 15u);
-    *reinterpret_cast<Raw<T>*>(&tile[row][swz(row, cc * 8)]) = raw[j];
+    *reinterpret_cast<Raw<T>*>(&tile[row][swz(row, cc * 8)]) = cur[j];
     if constexpr (ROW) {
-      Raw<T> rr = raw[j];
+      Raw<T> rr = cur[j];
       if constexpr (RHT) flip(rr, flips);
       float v[8];
       to_f32(rr, v);
@@ -174,63 +175,64 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
       }
     }
   }
-  if constexpr (!COL) return;
   __syncthreads();
 
   // ---- phase 2: column pairs over 32 rows. Lanes 4j .. 4j+3 of a wave hold the
   // four 32-row groups of one column pair, so a wave's store instruction writes 16
   // columns x 64 contiguous bytes.
-  const int cp = (int)(t >> 2);
-  const int h = (int)(t & 3u);
-  float v0[32], v1[32];
+  if constexpr (COL) {
+    const int cp = (int)(t >> 2);
+    const int h = (int)(t & 3u);
+    float v0[32], v1[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
-    const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) : 0u;
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]) ^
-                         (s ? 0x80008000u : 0u);
-      v0[i] = as_f(w << 16);
-      v1[i] = as_f(w & 0xFFFF0000u);
-    } else {
-      const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]);
-      v0[i] = as_f(as_u(w.x) ^ (s << 31));
-      v1[i] = as_f(as_u(w.y) ^ (s << 31));
+    for (int i = 0; i < 32; ++i) {
+      // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
+      const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) : 0u;
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w =
+            *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]) ^ (s ? 0x80008000u : 0u);
+        v0[i] = as_f(w << 16);
+        v1[i] = as_f(w & 0xFFFF0000u);
+      } else {
+        const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]);
+        v0[i] = as_f(as_u(w.x) ^ (s << 31));
+        v1[i] = as_f(as_u(w.y) ^ (s << 31));
+      }
     }
-  }
-  if constexpr (RHT) {
-    h16_local(v0);
-    h16_local(v0 + 16);
-    h16_local(v1);
-    h16_local(v1 + 16);
-  }
-  const int vrows = nr - h * 32;  // valid rows of this 32-row group
-  if (vrows <= 0) return;
+    if constexpr (RHT) {
+      h16_local(v0);
+      h16_local(v0 + 16);
+      h16_local(v1);
+      h16_local(v1 + 16);
+    }
+    const int vrows = nr - h * 32;  // valid rows of this 32-row group
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float* v = k ? v1 : v0;
-    const int64_t col = c0 + cp * 2 + k;
-    if (col >= c0 + nc) continue;
-    const int64_t grow0 = p.row0 + r0 + h * 32;  // first row of the group in the whole tensor
-    uint32_t u[32];
-    if constexpr (SR) philox_words<32>(p.sr_offset + (uint64_t)(col * p.total_rows + grow0), p.sr_seed, u);
-    uint8_t* cdst = p.codes_col + col * p.ld_col_codes + grow0 / 2;
-    uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
-    if constexpr (FMT == kMX) {
-      uint32_t out[4];
-      const uint32_t byte = mx_encode32<SR, RHT ? 2 : 0>(v, u, out);
-      *reinterpret_cast<uint4*>(cdst) = make_uint4(out[0], out[1], out[2], out[3]);
-      sdst[grow0 / 32] = (uint8_t)byte;
-    } else {
-      uint32_t out[4];
-      const uint32_t b0 = nv_encode16<SR>(v, u, nt, out);
-      const uint32_t b1 = nv_encode16<SR>(v + 16, u + 16, nt, out + 2);
-      // 8-byte stores: rows % 16 == 0 only guarantees 8-byte aligned column runs
-      *reinterpret_cast<uint2*>(cdst) = make_uint2(out[0], out[1]);
-      sdst[grow0 / 16] = (uint8_t)b0;
-      if (vrows >= 32) {
-        *reinterpret_cast<uint2*>(cdst + 8) = make_uint2(out[2], out[3]);
-        sdst[grow0 / 16 + 1] = (uint8_t)b1;
+    for (int k = 0; k < 2; ++k) {
+      const float* v = k ? v1 : v0;
+      const int64_t col = c0 + cp * 2 + k;
+      if (vrows > 0 && cp * 2 + k < nc) {
+        const int64_t grow0 = p.row0 + r0 + h * 32;  // first row of the group in the whole tensor
+        uint32_t u[32];
+        if constexpr (SR) philox_words<32>(p.sr_offset + (uint64_t)(col * p.total_rows + grow0), p.sr_seed, u);
+        uint8_t* cdst = p.codes_col + col * p.ld_col_codes + grow0 / 2;
+        uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
+        if constexpr (FMT == kMX) {
+          uint32_t out[4];
+          const uint32_t byte = mx_encode32<SR, RHT ? 2 : 0>(v, u, out);
+          *reinterpret_cast<uint4*>(cdst) = make_uint4(out[0], out[1], out[2], out[3]);
+          sdst[grow0 / 32] = (uint8_t)byte;
+        } else {
+          uint32_t out[4];
+          const uint32_t b0 = nv_encode16<SR>(v, u, nt, out);
+          const uint32_t b1 = nv_encode16<SR>(v + 16, u + 16, nt, out + 2);
+          // 8-byte stores: rows % 16 == 0 only guarantees 8-byte aligned column runs
+          *reinterpret_cast<uint2*>(cdst) = make_uint2(out[0], out[1]);
+          sdst[grow0 / 16] = (uint8_t)b0;
+          if (vrows >= 32) {
+            *reinterpret_cast<uint2*>(cdst + 8) = make_uint2(out[2], out[3]);
+            sdst[grow0 / 16 + 1] = (uint8_t)b1;
+          }
+        }
       }
     }
   }
@@ -238,8 +240,9 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
 
 template <typename T, int FMT, bool SR, bool RHT>
 static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
-  // slabs keep the tile count of one launch well inside the grid limit
-  const int64_t max_rows = (int64_t)kTileR * 65536;
+  // slabs of at most 2^22 tiles (cols <= 2^30 gives at most 2^23 tiles per tile row)
+  const int64_t tiles_per_row = (a.cols + kTileC - 1) / kTileC;
+  const int64_t max_rows = (int64_t)kTileR * std::max<int64_t>(1, ((int64_t)1 << 22) / tiles_per_row);
   for (int64_t s0 = 0; s0 < a.rows; s0 += max_rows) {
     const int64_t nr = std::min(max_rows, a.rows - s0);
     TileParams p;

@@ -63,6 +63,8 @@ def q(**kw):
     (dict(cols=48), mxq.MXQ_ESHAPE),             # not a multiple of 32
     (dict(ldx=32), mxq.MXQ_ESHAPE),
     (dict(axis=2, rows=48), mxq.MXQ_ESHAPE),
+    (dict(rows=1, cols=2 ** 31, ldx=2 ** 31), mxq.MXQ_ESHAPE),   # more than 2^30 columns
+    (dict(rows=2 ** 21, cols=2 ** 20, ldx=2 ** 20), mxq.MXQ_ESHAPE),  # more than 2^40 elements
     (dict(x=FAKE + 8), mxq.MXQ_EALIGN),
     (dict(ldx=68), mxq.MXQ_EALIGN),              # 136-byte rows
     (dict(cr=FAKE + 4), mxq.MXQ_EALIGN),
@@ -85,3 +87,5 @@ def test_other_entry_points_validation():
     assert L.mxq_rht_quantize(FAKE, 0, 4, 64, 64, 1, 1, 0, 0, 0, 0, FAKE, FAKE, None, None, FAKE, FAKE,
                               None) == mxq.MXQ_EUNSUPPORTED
     assert L.mxq_amax(FAKE, 0, 4, 64, 64, None, None) == mxq.MXQ_EINVAL
+    assert L.mxq_amax(FAKE, 0, 1, 2 ** 31, 2 ** 31, FAKE, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_dequantize(FAKE, FAKE, 0, 1, 2 ** 31, None, FAKE, 0, None) == mxq.MXQ_ESHAPE
