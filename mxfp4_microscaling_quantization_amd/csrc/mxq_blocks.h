@@ -132,10 +132,16 @@ __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t 
   uint32_t packed = 0;
   if constexpr (SR) {
     const float inv = as_f((254u - b - kShift) << 23);  // 2^-(E + kShift), exact
+    // y is exact; only the rounding of y + 1 (half a unit of F) can mislead the
+    // carry, so a window of K = 1 suffices
     float q[8];
+    uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      q[i] = as_f(as_u(e2m1_sr_value(fabsf(v[i]) * inv, u[i])) | (as_u(v[i]) & 0x80000000u));
+    for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_carry<1>(fabsf(v[i]) * inv, u[i], low), v[i]);
+    if (low < 2u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_value(fabsf(v[i]) * inv, u[i]), v[i]);
+    }
     packed = fp4x8_from_f32(q, 1.0f);
   } else {
     packed = fp4x8_from_f32(v, e8m0_operand(b + kShift));

@@ -235,6 +235,26 @@ __device__ __forceinline__ float e2m1_sr_value(float y, uint32_t u) {
 
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) { return e2m1_rne(e2m1_sr_value(y, u)); }
 
+// The same stochastic rounding decided by a carry. Adding 1 to y < 1 moves the grid
+// 0, 0.5, 1 onto 1, 1.5, 2, so every grid interval is one fp32 mantissa bit wide.
+// F, the 22 bits under that bit, is the position inside the interval in units of
+// 2^-22 of the gap, and T = 64 r + 32 is the threshold (r + 1/2) / 2^16 in the same
+// units. Adding 2^22 - 1 - T + K to the bits carries into the kept bit iff
+// F >= T + 1 - K. For F in [T + 1 - K, T + 1 + K) the low 22 bits of the sum are
+// below 2K: there an error of F below K units (y inexact, or the rounding of y + 1)
+// could flip the decision, so the caller keeps the running minimum `low` of those
+// bits and decides the elements exactly when it ends below 2K. Result: the grid
+// value, at most 6.
+template <uint32_t K>
+__device__ __forceinline__ float e2m1_sr_carry(float y, uint32_t u, uint32_t& low) {
+  const float off = y < 1.0f ? 1.0f : 0.0f;
+  const uint32_t d = ((u >> 10) & 0x3FFFC0u) ^ 0x3FFFC0u;  // 2^22 - 64 - 64 r
+  const uint32_t s = as_u(y + off) + d + (31u + K);
+  low = min(low, s & 0x3FFFFFu);
+  const float q = as_f(s & 0xFFC00000u) - off;
+  return as_f(min(as_u(q), 0x40C00000u));
+}
+
 // ---------------------------------------------------------------------------
 // Unsigned division of i < 2^30 by an invariant d >= 1: q = (i * m) >> s with
 // l = ceil(log2 d), s = 30 + l, m = ceil(2^s / d) < 2^31 + 1.
@@ -415,16 +435,24 @@ __device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t*
   float q[8];
   if (t.et >= -80) {
     const float inv = ldexpf(r, -t.et);
+    // y carries a relative error below 2^-21 (reciprocal, two products): at most a
+    // few units of F, well inside the window K = 16 of the carry decision
+    uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float ax = fabsf(v[i]);
-      const float y = ax * inv;
-      float lo, step;
-      e2m1_floor_step(y, lo, step);
-      // (lo + step (r + 1/2) 2^-16) s_b, exact: written as fma(step s_b, 1 + off, (lo - step) s_b)
-      const float c = fmaf(step * sb, sr_offset16_plus1(u[i]), (lo - step) * sb);
-      const bool up = fmaf(c, t.st, -ax) < 0.0f;
-      q[i] = with_sign_of(fminf(up ? lo + step : lo, 6.0f), v[i]);
+    for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_carry<16>(fabsf(v[i]) * inv, u[i], low), v[i]);
+    if (low < 32u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ax = fabsf(v[i]);
+        const float y = ax * inv;
+        float lo, step;
+        e2m1_floor_step(y, lo, step);
+        // threshold (lo + step (r + 1/2) 2^-16) s_b, exact (at most 23 significant
+        // bits); the sign of c s_t - |x| decides
+        const float c = fmaf(step, sr_offset16_plus1(u[i]), lo - step) * sb;
+        const bool up = fmaf(c, t.st, -ax) < 0.0f;
+        q[i] = with_sign_of(fminf(up ? lo + step : lo, 6.0f), v[i]);
+      }
     }
   } else {
 #pragma unroll

@@ -66,14 +66,17 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* 
   const uint32_t byte = mx_byte<kShift>(as_u(absmax32(v)));
   const uint32_t b = min(byte, 252u);
   if constexpr (SR) {
-    const float inv = as_f((254u - b - kShift) << 23);
+    const float inv = as_f((254u - b - kShift) << 23);  // exact: a window of K = 1 suffices
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       float q[8];
+      uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = d * 8 + i;
-        q[i] = as_f(as_u(e2m1_sr_value(fabsf(v[e]) * inv, u[e])) | (as_u(v[e]) & 0x80000000u));
+      for (int i = 0; i < 8; ++i)
+        q[i] = with_sign_of(e2m1_sr_carry<1>(fabsf(v[d * 8 + i]) * inv, u[d * 8 + i], low), v[d * 8 + i]);
+      if (low < 2u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_value(fabsf(v[d * 8 + i]) * inv, u[d * 8 + i]), v[d * 8 + i]);
       }
       out[d] = byte == 255u ? 0u : fp4x8_from_f32(q, 1.0f);
     }
