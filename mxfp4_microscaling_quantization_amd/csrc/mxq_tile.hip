@@ -1,15 +1,18 @@
 // Column-wise (and fused row + column) quantisation from one read of the input.
 //
-// A 256-thread workgroup owns a 128 x 128 tile. Phase 1: every thread loads eight
-// 16-byte chunks (a wave reads four 256-byte row segments per instruction),
-// quantises them row-wise if asked (blocks along the row span a DPP quad, exactly
-// as in the row kernel) and parks the raw values in LDS. Phase 2: thread t owns
-// the column pair 2*(t/4), 2*(t/4)+1 over rows 32*(t%4) .. +31 and reads them as
-// one dword (bf16) per row. The LDS tile is XOR-swizzled so that these reads hit
-// all 32 banks. The optional Hadamard transform runs along the rows in registers,
-// each column's 32 codes leave as one 16-byte store, and the four lanes of a
-// column pair sit side by side, so each store instruction writes 64 contiguous
-// bytes per column.
+// A 256-thread workgroup owns a 128 x 128 tile (64 x 128 for fp32 input, so the
+// LDS tile is 32 KB either way). Phase 1: every thread loads 16-byte chunks (a wave
+// reads four 256-byte row segments per instruction), quantises them row-wise if
+// asked (blocks along the row span a DPP quad, exactly as in the row kernel) and
+// parks the raw values in LDS. Phase 2: a task is one column over 32 rows; the
+// 32-row groups of a column sit on neighbouring lanes, so each store instruction
+// writes 64 contiguous bytes (16 bytes per lane) for each of 16 columns. The LDS
+// tile is XOR-swizzled so that phase 2 reads hit all 32 banks, and the optional
+// Hadamard transform runs along the rows in registers.
+//
+// Workgroups are dealt to the eight XCDs in turn; pairs of vertically adjacent
+// tiles go to one XCD in consecutive turns, so both halves of a 128-byte line of
+// column codes are written through the same L2.
 #include <algorithm>
 
 #include "mxq_blocks.h"
@@ -18,8 +21,14 @@
 namespace mxq {
 
 constexpr int kTileThreads = 256;
-constexpr int kTileR = 128;
-constexpr int kTileC = 128;
+// Tile shape per input type.
+template <typename T>
+struct TileShape {
+  static constexpr int R = sizeof(T) == 2 ? 128 : 64;
+  static constexpr int C = 128;     // a multiple of 64
+  static constexpr int G = R / 32;  // 32-row groups of a column
+};
+constexpr int kVGroup = 2;  // vertically adjacent tiles dispatched together
 
 struct TileParams {
   const void* x;
@@ -27,7 +36,8 @@ struct TileParams {
   int64_t rows, cols;          // slab extent
   int64_t total_rows;          // whole tensor (column-wise SR index and strides)
   int64_t row0;                // slab's first row in the whole tensor
-  uint32_t tiles_c;            // tiles across the columns
+  uint32_t tiles_r, tiles_c;   // tiles down and across the slab
+  uint32_t groups;             // groups of kVGroup vertically adjacent tiles
   uint32_t sign_mask;
   uint64_t sr_seed, sr_offset;
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
@@ -117,14 +127,19 @@ __device__ __forceinline__ uint32_t nv_encode16(const float* v, const uint32_t* 
 }
 
 // LDS column index of element column c in tile row r. Phase 2 reads, at one
-// instant, column pairs 16a .. 16a+15 in rows 32h + i for h = 0..3; XOR-ing the
-// column-pair index with 8h (bits 3-4) spreads those 64 lanes over all 32 banks.
-// Groups of four column pairs (one 16-byte chunk of bf16) stay contiguous.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 5) & 3) << 4); }
+// instant, columns 16a .. 16a+15 in rows 32h + i for h = 0..3 (rows 32 apart start
+// on the same bank); XOR-ing the column with 16h spreads those 64 lanes over all
+// 32 banks (bf16; fp32 rows span two bank sweeps and see at most two-way sharing).
+// Chunks of eight columns stay contiguous.
+template <int G>
+__device__ __forceinline__ int swz(int r, int c) {
+  return c ^ (((r >> 5) & (G - 1)) * (64 / G));
+}
 
 template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
 __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams p) {
   // LDS tile of raw input values, row-major [128][128], XOR-swizzled columns
+  constexpr int kTileR = TileShape<T>::R, kTileC = TileShape<T>::C, kRowGroups = TileShape<T>::G;
   __shared__ T tile[kTileR][kTileC];
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t t = threadIdx.x;
@@ -135,10 +150,19 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   }
   SignFlips flips;
   if constexpr (RHT && ROW) flips = make_flips<T>(p.sign_mask, t & 1u);
-  constexpr int kChunks = kTileR * kTileC / 8 / kTileThreads;  // 8 per thread
+  constexpr int kChunks = kTileR * kTileC / 8 / kTileThreads;  // chunks per thread
+  constexpr int kChunksPerRow = kTileC / 8;
 
   // tile origin and extent within the slab
-  const uint32_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x - tr * p.tiles_c;
+  // Workgroups are dealt to the eight XCDs in turn (blockIdx mod 8). The kVGroup
+  // tiles of one vertical group go to the same XCD in consecutive turns, so the
+  // column codes they share in a 128-byte line meet in one L2.
+  const uint32_t xcd = blockIdx.x & 7u, slot = blockIdx.x >> 3;
+  const uint32_t g = (slot / kVGroup) * 8u + xcd;
+  if (g >= p.groups) return;
+  const uint32_t gr = g / p.tiles_c, tc = g - gr * p.tiles_c;
+  const uint32_t tr = gr * kVGroup + slot % kVGroup;
+  if (tr >= p.tiles_r) return;
   const int64_t r0 = (int64_t)tr * kTileR, c0 = (int64_t)tc * kTileC;
   const int nr = (int)std::min<int64_t>(kTileR, p.rows - r0);
   const int nc = (int)std::min<int64_t>(kTileC, p.cols - c0);
@@ -146,8 +170,8 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     const uint32_t q = t + j * kTileThreads;
-    const int row = (int)(q >> 4), cc = (int)(q & 15u);
-    if (row < nr && cc * 8 < nc) load_raw(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, cur[j]);
+    const int row = (int)(q / kChunksPerRow), cc = (int)(q % kChunksPerRow);
+    if (row < nr && cc * 8 < nc) load_raw<ROW>(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, cur[j]);
     else zero_raw(cur[j]);
   }
 
@@ -155,8 +179,8 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
     const uint32_t q = t + j * kTileThreads;
-    const int row = (int)(q >> 4), cc = (int)(q & 15u);
-    *reinterpret_cast<Raw<T>*>(&tile[row][swz(row, cc * 8)]) = cur[j];
+    const int row = (int)(q / kChunksPerRow), cc = (int)(q % kChunksPerRow);
+    *reinterpret_cast<Raw<T>*>(&tile[row][swz<kRowGroups>(row, cc * 8)]) = cur[j];
     if constexpr (ROW) {
       Raw<T> rr = cur[j];
       if constexpr (RHT) flip(rr, flips);
@@ -180,40 +204,30 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   }
   __syncthreads();
 
-  // ---- phase 2: column pairs over 32 rows. Lanes 4j .. 4j+3 of a wave hold the
-  // four 32-row groups of one column pair, so a wave's store instruction writes 16
-  // columns x 64 contiguous bytes.
+  // ---- phase 2: one column over 32 rows per task, (kTileC x kRowGroups) tasks.
+  // Neighbouring lanes hold the 32-row groups of one column, so a store
+  // instruction writes kRowGroups x 16 contiguous bytes per column.
   if constexpr (COL) {
-    const int cp = (int)(t >> 2);
-    const int h = (int)(t & 3u);
-    float v0[32], v1[32];
+#pragma unroll 1
+    for (int k = t; k < kTileC * kRowGroups; k += kTileThreads) {
+      const int c = k / kRowGroups;
+      const int h = k % kRowGroups;
+      float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
-      const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) : 0u;
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t w =
-            *reinterpret_cast<const uint32_t*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]) ^ (s ? 0x80008000u : 0u);
-        v0[i] = as_f(w << 16);
-        v1[i] = as_f(w & 0xFFFF0000u);
-      } else {
-        const float2 w = *reinterpret_cast<const float2*>(&tile[h * 32 + i][swz(h * 32 + i, cp * 2)]);
-        v0[i] = as_f(as_u(w.x) ^ (s << 31));
-        v1[i] = as_f(as_u(w.y) ^ (s << 31));
+      for (int i = 0; i < 32; ++i) {
+        // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
+        const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) << 31 : 0u;
+        const int r = h * 32 + i;
+        if constexpr (sizeof(T) == 2) v[i] = as_f(((uint32_t)tile[r][swz<kRowGroups>(r, c)] << 16) ^ s);
+        else v[i] = as_f(as_u(tile[r][swz<kRowGroups>(r, c)]) ^ s);
       }
-    }
-    if constexpr (RHT) {
-      h16_local(v0);
-      h16_local(v0 + 16);
-      h16_local(v1);
-      h16_local(v1 + 16);
-    }
-    const int vrows = nr - h * 32;  // valid rows of this 32-row group
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const float* v = k ? v1 : v0;
-      const int64_t col = c0 + cp * 2 + k;
-      if (vrows > 0 && cp * 2 + k < nc) {
+      if constexpr (RHT) {
+        h16_local(v);
+        h16_local(v + 16);
+      }
+      const int vrows = nr - h * 32;  // valid rows of this 32-row group
+      const int64_t col = c0 + c;
+      if (vrows > 0 && c < nc) {
         const int64_t grow0 = p.row0 + r0 + h * 32;  // first row of the group in the whole tensor
         uint32_t u[32];
         if constexpr (SR) philox_words<32>(p.sr_offset + (uint64_t)(col * p.total_rows + grow0), p.sr_seed, u);
@@ -243,6 +257,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
 
 template <typename T, int FMT, bool SR, bool RHT>
 static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
+  constexpr int kTileR = TileShape<T>::R, kTileC = TileShape<T>::C;
   // slabs of at most 2^22 tiles (cols <= 2^30 gives at most 2^23 tiles per tile row)
   const int64_t tiles_per_row = (a.cols + kTileC - 1) / kTileC;
   const int64_t max_rows = (int64_t)kTileR * std::max<int64_t>(1, ((int64_t)1 << 22) / tiles_per_row);
@@ -258,7 +273,9 @@ static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
     p.row0 = a.row0 + s0;
     const int64_t tiles_r = (nr + kTileR - 1) / kTileR;
     const int64_t tiles_c = (a.cols + kTileC - 1) / kTileC;
+    p.tiles_r = (uint32_t)tiles_r;
     p.tiles_c = (uint32_t)tiles_c;
+    p.groups = (uint32_t)(((tiles_r + kVGroup - 1) / kVGroup) * tiles_c);
     p.sign_mask = a.sign_mask;
     p.sr_seed = a.sr_seed;
     p.sr_offset = a.sr_offset;
@@ -271,7 +288,7 @@ static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
     p.ld_col_scales = a.ld_col_scales;
     p.amax = a.amax;
     p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
-    const uint32_t grid = (uint32_t)(tiles_r * tiles_c);
+    const uint32_t grid = 8u * kVGroup * ((p.groups + 7u) / 8u);
     if (a.want_row && a.want_col)
       hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, true, true>), dim3(grid),
                          dim3(kTileThreads), 0, st, p);
