@@ -102,12 +102,54 @@ def cpu_baseline(x_cpu, q8_cpu, s_cpu, rows: int):
     return step_bytes / dt / 1e9, dt
 
 
+# Roofline peaks of one MI355X: HBM3E bandwidth, and the vector ALU rate for 32-bit
+# integer/fp32 operations without packing (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Stochastic rounding is bound by its Philox4x32-10 stream, not by HBM. Algorithmic
+# operations per element: Philox (10 rounds of 2 32x32->64 multiplies and 4 XORs per
+# 4 words = 15), then scaling, grid floor, threshold compare and select (4).
+SR_OPS_PER_ELEMENT = 19
+ALU_BOUND = {"nvfp4_quantize_sr"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+SOURCES = ("include/mxq.h", "mxfp4_microscaling_quantization_amd/csrc")
+
+
+def source_digest() -> str:
+    """SHA-256 over the library sources: PMC traffic is reported only for the kernel
+    version the counters were taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    paths = []
+    for rel in SOURCES:
+        p = os.path.join(ROOT, rel)
+        if os.path.isdir(p):
+            paths += sorted(os.path.join(p, f) for f in os.listdir(p) if f.endswith((".hip", ".h")))
+        else:
+            paths.append(p)
+    for p in paths:
+        h.update(os.path.relpath(p, ROOT).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("source_sha256") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--kernel-reps", type=int, default=50, help="launches per kernel for per-kernel timing")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps (also bring the clocks up)")
+    ap.add_argument("--kernel-reps", type=int, default=20, help="back-to-back launches per kernel for its duration")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the oracle sample (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -133,8 +175,9 @@ def main() -> int:
             fn()
     torch.cuda.synchronize()
 
-    # whole-step throughput over exactly `steps` steps
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region: exactly `steps` steps, bracketed by events on torch's current stream.
+    E = torch.cuda.Event
+    start, stop = E(enable_timing=True), E(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
@@ -150,12 +193,14 @@ def main() -> int:
     print(f"[bench] {args.steps} steps: {gpu_ms:.3f} ms on the stream ({wall * 1e3:.3f} ms wall), "
           f"{step_bytes / 1e6:.1f} MB per step", file=sys.stderr, flush=True)
 
-    # per-kernel average launch duration: event pair around `kernel_reps` launches
+    # Per-kernel average launch duration: `kernel_reps` back-to-back launches of one
+    # kernel between two events on the stream the kernels run on, so the events' own
+    # cost is spread over the launches. (Inside the step a kernel also absorbs the
+    # write-back of its predecessor's output; the step time above includes that.)
     per = {}
     for name, fn, b in kernels:
         fn()
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0, s1 = E(enable_timing=True), E(enable_timing=True)
         s0.record()
         for _ in range(args.kernel_reps):
             fn()
@@ -171,7 +216,7 @@ def main() -> int:
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = E(enable_timing=True), E(enable_timing=True)
     c0.record()
     for _ in range(10):
         dst.copy_(src)
@@ -180,10 +225,21 @@ def main() -> int:
     copy_gbs = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) / 1e3) / 1e9
     del src, dst
     print(f"[bench] torch D2D copy of 1 GiB: {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
     dom = max(per, key=lambda k: per[k]["us"])
-    roof = {"kernel": dom, "bound": "hbm", "achieved": per[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(per[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
-            "bytes_per_launch": per[dom]["bytes"], "avg_launch_us": per[dom]["us"]}
+    d = per[dom]
+    traffic = measured_traffic(dom)
+    if dom in ALU_BOUND:
+        ops = SR_OPS_PER_ELEMENT * R * C
+        tops = ops / (d["us"] * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "alu", "achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
+                "ops_per_launch": ops, "ops_per_element": SR_OPS_PER_ELEMENT, "avg_launch_us": d["us"],
+                "hbm_GB_s": d["GB_s"], "hbm_frac": d["frac_hbm_peak"], "bytes_per_launch": d["bytes"]}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["frac_hbm_peak"], "traffic": traffic, "bytes_per_launch": d["bytes"],
+                "avg_launch_us": d["us"]}
 
     cpu = None
     if args.cpu_rows > 0:
