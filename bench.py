@@ -29,45 +29,60 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 
 
-def build_step(x, dev):
+def build_step(x, dev, sets: int = 3):
+    """The eight kernels of one step, over `sets` independent buffer sets.
+
+    Within a set every kernel reads its own copy of its input (identical data), and
+    steps rotate through the sets, so no launch finds its input in the 256 MB MALL or
+    the L2: every input byte comes from HBM (a set is about 2.2 GB). Returns
+    (kernels, fp8 input) where kernels[i] = (name, fn(set), algorithmic bytes)."""
     import torch
 
     from mxfp4_microscaling_quantization_amd import mxq, workloads
 
     R, C = x.shape
     N = R * C
-    q8, s128 = workloads.fp8_from_bf16(x)  # the FP8 producer's output (input of fp8_to_mxfp4)
+    q8_0, s128_0 = workloads.fp8_from_bf16(x.cpu())
     mask = mxq.mxq_rht_signs(4)
     u8 = torch.uint8
-    qz = mxq.Quantized(torch.empty((R, C // 2), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
-                       None, None, None)
-    yb = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
-    c8 = (torch.empty((R, C // 2), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev))
-    f8 = (torch.empty((R, C), dtype=u8, device=dev), torch.empty((R, C // 128), dtype=torch.float32, device=dev))
-    rq = mxq.Quantized(torch.empty((R, C // 2), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
-                       torch.empty((C, R // 2), dtype=u8, device=dev), torch.empty((C, R // 32), dtype=u8, device=dev),
-                       None)
-    amax = torch.empty((1,), dtype=torch.float32, device=dev)
-    nq = mxq.Quantized(torch.empty((R, C // 2), dtype=u8, device=dev), torch.empty((R, C // 16), dtype=u8, device=dev),
-                       None, None, torch.empty((1,), dtype=torch.float32, device=dev))
-    sq = mxq.Quantized(torch.empty((R, C // 2), dtype=u8, device=dev), torch.empty((R, C // 16), dtype=u8, device=dev),
-                       None, None, torch.empty((1,), dtype=torch.float32, device=dev))
+
+    def e(*shape, dtype=u8):
+        return torch.empty(shape, dtype=dtype, device=dev)
+
+    S = []
+    for _ in range(sets):
+        st = {"xa": x.clone(), "xr": x.clone(), "xm": x.clone(), "xn": x.clone(), "xs": x.clone(),
+              "q8": q8_0.to(dev), "s128": s128_0.to(dev)}
+        st["deq_in"] = mxq.mxq_quantize(st["xa"], "mxfp4", "row")
+        st["f8_in"] = mxq.mxq_fp8_to_mxfp4(st["q8"], st["s128"])
+        st["qz"] = mxq.Quantized(e(R, C // 2), e(R, C // 32), None, None, None)
+        st["yb"] = e(R, C, dtype=torch.bfloat16)
+        st["c8"] = (e(R, C // 2), e(R, C // 32))
+        st["f8"] = (e(R, C), e(R, C // 128, dtype=torch.float32))
+        st["rq"] = mxq.Quantized(e(R, C // 2), e(R, C // 32), e(C, R // 2), e(C, R // 32), None)
+        st["amax"] = e(1, dtype=torch.float32)
+        st["nq"] = mxq.Quantized(e(R, C // 2), e(R, C // 16), None, None, e(1, dtype=torch.float32))
+        st["sq"] = mxq.Quantized(e(R, C // 2), e(R, C // 16), None, None, e(1, dtype=torch.float32))
+        S.append(st)
+    torch.cuda.synchronize()
     mx_b = 2 * N + N // 2 + N // 32
     f8_b = N + 4 * (N // 128) + N // 2 + N // 32
+    nv_b = 2 * N + N // 2 + N // 16 + 4
     kernels = [
-        ("mxfp4_quantize", lambda: mxq.mxq_quantize(x, "mxfp4", "row", out=qz), mx_b),
-        ("mxfp4_dequantize", lambda: mxq.mxq_dequantize(qz.codes_row, qz.scales_row, "mxfp4", out=yb), mx_b),
-        ("fp8_to_mxfp4", lambda: mxq.mxq_fp8_to_mxfp4(q8, s128, out=c8), f8_b),
-        ("mxfp4_to_fp8", lambda: mxq.mxq_mxfp4_to_fp8(c8[0], c8[1], out=f8), f8_b),
-        ("rht_mxfp4_rowcol", lambda: mxq.mxq_rht_quantize(x, mask, "mxfp4", "both", out=rq),
+        ("mxfp4_quantize", lambda k: mxq.mxq_quantize(S[k]["xa"], "mxfp4", "row", out=S[k]["qz"]), mx_b),
+        ("mxfp4_dequantize", lambda k: mxq.mxq_dequantize(S[k]["deq_in"].codes_row, S[k]["deq_in"].scales_row,
+                                                          "mxfp4", out=S[k]["yb"]), mx_b),
+        ("fp8_to_mxfp4", lambda k: mxq.mxq_fp8_to_mxfp4(S[k]["q8"], S[k]["s128"], out=S[k]["c8"]), f8_b),
+        ("mxfp4_to_fp8", lambda k: mxq.mxq_mxfp4_to_fp8(S[k]["f8_in"][0], S[k]["f8_in"][1], out=S[k]["f8"]), f8_b),
+        ("rht_mxfp4_rowcol", lambda k: mxq.mxq_rht_quantize(S[k]["xr"], mask, "mxfp4", "both", out=S[k]["rq"]),
          2 * N + 2 * (N // 2 + N // 32)),
-        ("nvfp4_amax", lambda: mxq.mxq_amax(x, out=amax), 2 * N + 4),
-        ("nvfp4_quantize_rne", lambda: mxq.mxq_quantize(x, "nvfp4", "row", amax=amax, out=nq),
-         2 * N + N // 2 + N // 16 + 4),
-        ("nvfp4_quantize_sr", lambda: mxq.mxq_quantize(x, "nvfp4", "row", "sr", sr_seed=7, amax=amax, out=sq),
-         2 * N + N // 2 + N // 16 + 4),
+        ("nvfp4_amax", lambda k: mxq.mxq_amax(S[k]["xm"], out=S[k]["amax"]), 2 * N + 4),
+        ("nvfp4_quantize_rne", lambda k: mxq.mxq_quantize(S[k]["xn"], "nvfp4", "row", amax=S[k]["amax"],
+                                                          out=S[k]["nq"]), nv_b),
+        ("nvfp4_quantize_sr", lambda k: mxq.mxq_quantize(S[k]["xs"], "nvfp4", "row", "sr", sr_seed=7,
+                                                         amax=S[k]["amax"], out=S[k]["sq"]), nv_b),
     ]
-    return kernels, (q8, s128)
+    return kernels, (q8_0, s128_0)
 
 
 def cpu_baseline(x_cpu, q8_cpu, s_cpu, rows: int):
@@ -144,6 +159,95 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes")
 
 
+def config_report(dev, reps: int = 30) -> list:
+    """Each configuration of the pages' workloads at its own shape: per-kernel average
+    duration over `reps` back-to-back launches (after a warm-up), GB/s, elements/s and
+    % of the HBM peak. Launches rotate through copies of the buffers whose total
+    exceeds the 256 MB MALL, so every input is read from HBM."""
+    import torch
+
+    from mxfp4_microscaling_quantization_amd import mxq, workloads
+
+    E = torch.cuda.Event
+
+    def timed(fn, n):
+        for k in range(5):
+            fn(k % n)
+        torch.cuda.synchronize()
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        for k in range(reps):
+            fn(k % n)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    out = []
+
+    def row(cfg, name, fn, n, nbytes, elems):
+        us = timed(fn, n)
+        r = {"config": cfg, "kernel": name, "us": round(us, 3), "bytes": nbytes, "GB_s": round(nbytes / us / 1e3, 1),
+             "elements_per_s": round(elems / (us * 1e-6), 1), "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+             "buffer_sets": n}
+        print("[config] " + json.dumps(r), file=sys.stderr, flush=True)
+        out.append(r)
+
+    def copies(t, n):
+        return [t.to(dev) for _ in range(n)]
+
+    # warm the clocks up
+    w = workloads.mxfp4_rowwise_moe().x.to(dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        mxq.mxq_quantize(w, "mxfp4", "row", "sr", sr_seed=1)
+        torch.cuda.synchronize()
+    del w
+    for cfg, n, wl in ((1, 64, workloads.mxfp4_rowwise_small()), (2, 3, workloads.mxfp4_rowwise_moe())):
+        xs = copies(wl.x, n)
+        R, C = wl.x.shape
+        N = R * C
+        qs = [mxq.mxq_quantize(x, "mxfp4", "row") for x in xs]
+        ys = [torch.empty_like(x) for x in xs]
+        b = 2 * N + N // 2 + N // 32
+        row(cfg, "mxfp4_quantize", lambda k: mxq.mxq_quantize(xs[k], "mxfp4", "row", out=qs[k]), n, b, N)
+        row(cfg, "mxfp4_dequantize",
+            lambda k: mxq.mxq_dequantize(qs[k].codes_row, qs[k].scales_row, "mxfp4", out=ys[k]), n, b, N)
+        del xs, qs, ys
+    n = 2
+    wl = workloads.fp8_moe_experts()
+    q8s, s128s = copies(wl.q8, n), copies(wl.s128, n)
+    N = wl.q8.numel()
+    c8s = [mxq.mxq_fp8_to_mxfp4(q8s[k], s128s[k]) for k in range(n)]
+    f8s = [mxq.mxq_mxfp4_to_fp8(*c8s[k]) for k in range(n)]
+    b = N + 4 * (N // 128) + N // 2 + N // 32
+    row(3, "fp8_to_mxfp4", lambda k: mxq.mxq_fp8_to_mxfp4(q8s[k], s128s[k], out=c8s[k]), n, b, N)
+    row(3, "mxfp4_to_fp8", lambda k: mxq.mxq_mxfp4_to_fp8(c8s[k][0], c8s[k][1], out=f8s[k]), n, b, N)
+    del q8s, s128s, c8s, f8s, wl
+    n = 3
+    wl = workloads.rht_gradients()
+    xs = copies(wl.x, n)
+    N = wl.x.numel()
+    mask = mxq.mxq_rht_signs(wl.rht_seed)
+    os_ = [mxq.mxq_rht_quantize(x, mask, "mxfp4", "both") for x in xs]
+    b = 2 * N + 2 * (N // 2 + N // 32)
+    row(4, "rht_mxfp4_rowcol", lambda k: mxq.mxq_rht_quantize(xs[k], mask, "mxfp4", "both", out=os_[k]), n, b, N)
+    row(4, "mxfp4_rowcol (no RHT)", lambda k: mxq.mxq_quantize(xs[k], "mxfp4", "both", out=os_[k]), n, b, N)
+    row(4, "rht_mxfp4_col", lambda k: mxq.mxq_rht_quantize(xs[k], mask, "mxfp4", "col", out=os_[k]), n,
+        b - N // 2 - N // 32, N)
+    del xs, os_, wl
+    wl = workloads.nvfp4_activations()
+    xs = copies(wl.x, n)
+    N = wl.x.numel()
+    amax = [mxq.mxq_amax(x) for x in xs]
+    os_ = [mxq.mxq_quantize(x, "nvfp4", "row", amax=a) for x, a in zip(xs, amax)]
+    b = 2 * N + N // 2 + N // 16 + 4
+    row(5, "nvfp4_amax", lambda k: mxq.mxq_amax(xs[k], out=amax[k]), n, 2 * N + 4, N)
+    row(5, "nvfp4_quantize_rne", lambda k: mxq.mxq_quantize(xs[k], "nvfp4", "row", amax=amax[k], out=os_[k]), n, b, N)
+    row(5, "nvfp4_quantize_sr", lambda k: mxq.mxq_quantize(xs[k], "nvfp4", "row", "sr", sr_seed=wl.sr_seed,
+                                                            amax=amax[k], out=os_[k]), n, b, N)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +255,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100, help="untimed steps (also bring the clocks up)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="back-to-back launches per kernel for its duration")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the oracle sample (0: skip)")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time every configuration at its own shape ([config] lines on stderr)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one MI355X: the quantisation kernels need no collectives and this "
@@ -167,12 +273,13 @@ def main() -> int:
     R, C = 16384, 7168
     x_cpu = workloads.moe_activations(R, C, 2)
     x = x_cpu.to(dev)
-    kernels, (q8, s128) = build_step(x, dev)
+    sets = 3
+    kernels, (q8, s128) = build_step(x, dev, sets)
     step_bytes = sum(b for _, _, b in kernels)
 
-    for _ in range(args.warmup):
+    for w in range(args.warmup):
         for _, fn, _ in kernels:
-            fn()
+            fn(w % sets)
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps, bracketed by events on torch's current stream.
@@ -181,9 +288,9 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
+    for k in range(args.steps):
         for _, fn, _ in kernels:
-            fn()
+            fn(k % sets)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -194,16 +301,17 @@ def main() -> int:
           f"{step_bytes / 1e6:.1f} MB per step", file=sys.stderr, flush=True)
 
     # Per-kernel average launch duration: `kernel_reps` back-to-back launches of one
-    # kernel between two events on the stream the kernels run on, so the events' own
-    # cost is spread over the launches. (Inside the step a kernel also absorbs the
-    # write-back of its predecessor's output; the step time above includes that.)
+    # kernel, rotating through the buffer sets, between two events on the stream the
+    # kernels run on, so the events' own cost is spread over the launches. (Inside the
+    # step a kernel also absorbs the write-back of its predecessor's output; the step
+    # time above includes that.)
     per = {}
     for name, fn, b in kernels:
-        fn()
+        fn(0)
         s0, s1 = E(enable_timing=True), E(enable_timing=True)
         s0.record()
-        for _ in range(args.kernel_reps):
-            fn()
+        for r in range(args.kernel_reps):
+            fn((r + 1) % sets)
         s1.record()
         torch.cuda.synchronize()
         us = s0.elapsed_time(s1) * 1e3 / args.kernel_reps
@@ -271,6 +379,10 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.configs:
+        del kernels
+        torch.cuda.empty_cache()
+        config_report(dev)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -18,14 +18,14 @@ struct Raw<float> {
   float4 a, b;
 };
 
-// One 8-element chunk. NT selects nontemporal loads: measured faster for the fused
-// row + column tile kernel, slower for the row kernels and the column-only tile.
-template <bool NT = false>
+// One 8-element chunk, by default with nontemporal loads: on inputs that come from
+// HBM (not from the 256 MB MALL) they stream measurably faster than plain loads.
+template <bool NT = true>
 __device__ __forceinline__ void load_raw(const uint16_t* x, size_t off, Raw<uint16_t>& r) {
   if constexpr (NT) r.w = load_nt(reinterpret_cast<const uint4*>(x + off));
   else r.w = *reinterpret_cast<const uint4*>(x + off);
 }
-template <bool NT = false>
+template <bool NT = true>
 __device__ __forceinline__ void load_raw(const float* x, size_t off, Raw<float>& r) {
   if constexpr (NT) {
     r.a = load_nt(reinterpret_cast<const float4*>(x + off));

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kF8Threads) void fp8_to_mxfp4_kernel(F8Params p) {
     q[j] = make_uint4(0, 0, 0, 0);
     s[j] = 0x3F800000u;
     if (c < p.chunks) {
-      q[j] = reinterpret_cast<const uint4*>(p.q8)[c];  // plain loads: measured faster here than nontemporal
+      q[j] = load_nt(reinterpret_cast<const uint4*>(p.q8) + c);
       s[j] = p.s128[c >> 3];
     }
   }
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kF8Threads) void mxfp4_to_fp8_kernel(F8BackParams p
     cw[j] = make_uint2(0, 0);
     gw[j] = 0;
     if (c < p.chunks) {
-      cw[j] = p.codes[c];
+      cw[j] = p.codes[c];  // plain loads: measured slightly faster here than nontemporal
       gw[j] = p.e8m0[c >> 3];
     }
   }

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   for (int j = 0; j < kChunks; ++j) {
     const uint32_t q = t + j * kTileThreads;
     const int row = (int)(q / kChunksPerRow), cc = (int)(q % kChunksPerRow);
-    if (row < nr && cc * 8 < nc) load_raw<ROW>(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, cur[j]);
+    if (row < nr && cc * 8 < nc) load_raw(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, cur[j]);
     else zero_raw(cur[j]);
   }
 
