@@ -28,6 +28,23 @@ __device__ __forceinline__ float4 load_nt(const float4* p) {
 }
 __device__ __forceinline__ uint32_t load_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 
+// Nontemporal vector stores, for outputs whose every store instruction writes whole
+// contiguous lines (measured faster on data that does not fit the caches). Pieces
+// of a line written by different instructions or workgroups, and single scale
+// bytes, stay plain stores so that the L2 can merge them.
+__device__ __forceinline__ void store_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+  __builtin_nontemporal_store(nt_u32x2{v.x, v.y}, reinterpret_cast<nt_u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(nt_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4*>(p));
+}
+__device__ __forceinline__ void store_nt(float4* p, float4 v) {
+  store_nt(reinterpret_cast<uint4*>(p), make_uint4(__float_as_uint(v.x), __float_as_uint(v.y),
+                                                    __float_as_uint(v.z), __float_as_uint(v.w)));
+}
+
 // DPP quad permutations (64-wide waves are split into quads of 4 lanes).
 constexpr int kQuadSwap1 = 0xB1;  // [1,0,3,2]: exchange with the neighbouring lane
 constexpr int kQuadSwap2 = 0x4E;  // [2,3,0,1]: exchange with the lane two away

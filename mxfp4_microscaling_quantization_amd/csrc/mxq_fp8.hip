@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kF8Threads) void fp8_to_mxfp4_kernel(F8Params p) {
     }
     if (byte == 255u) out[0] = out[1] = 0u;
     if (c < p.chunks) {
-      reinterpret_cast<uint2*>(p.codes)[c] = make_uint2(out[0], out[1]);
+      store_nt(reinterpret_cast<uint2*>(p.codes) + c, make_uint2(out[0], out[1]));
       if ((c & 1u) == 0u) p.e8m0[c >> 1] = (uint8_t)byte;
     }
   }
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kF8Threads) void mxfp4_to_fp8_kernel(F8BackParams p
       o[2 * h + 1] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
     }
     if (nan) o[0] = o[1] = o[2] = o[3] = 0x7F7F7F7Fu;
-    p.q8[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    store_nt(p.q8 + c, make_uint4(o[0], o[1], o[2], o[3]));
     if ((c & 7u) == 0u) p.s128[c >> 3] = nan ? 0x7FC00000u : (S ? (S << 23) : 0x00400000u);
   }
 }

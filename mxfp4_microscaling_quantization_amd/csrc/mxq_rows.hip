@@ -177,7 +177,7 @@ __device__ __forceinline__ uint32_t bf16_of_product(float a, float st_scaled, in
   return (sign >> 16) | (rnd >> 16);
 }
 
-template <int FMT, bool OUT_F32>
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
   const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
   float st = 0.0f, st_s = 0.0f;
@@ -203,30 +203,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
   for (int j = 0; j < kUnroll; ++j) {
     const uint32_t c = base + j * kThreads;
     if (c >= p.chunks) continue;
-    uint32_t out[8];
+    uint4 ov;
     if constexpr (FMT == kMX) {
       const uint32_t byte = sb[j];
       const float scale = e8m0_operand(min(byte, 254u));
       const bool nan = byte == 255u;
-      if constexpr (OUT_F32) {
-        const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 0);
-        const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 1);
-        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 2);
-        const f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 3);
-        const float vv[8] = {a.x, a.y, b.x, b.y, d.x, d.y, e.x, e.y};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = nan ? 0x7FC00000u : as_u(vv[i]);
-      } else {
-        uint32_t o[4];
-        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 0));
-        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 1));
-        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 2));
-        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 3));
-        uint4 ov = nan ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u)
-                       : make_uint4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<uint4*>(p.y)[c] = ov;
-        continue;
-      }
+      uint32_t o[4];
+      o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 0));
+      o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 1));
+      o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 2));
+      o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], scale, 3));
+      ov = nan ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u) : make_uint4(o[0], o[1], o[2], o[3]);
     } else {
       const uint32_t byte = sb[j];
       const bool nan = (byte & 0x7Fu) == 0x7Fu || !(fabsf(st) <= 3.40282347e38f);
@@ -242,47 +229,82 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
         a[2 * h] = d[h].x * sbv;  // exact: at most 6 significant bits
         a[2 * h + 1] = d[h].y * sbv;
       }
-      if constexpr (OUT_F32) {
+      // RN_bf16(RN_f32(a s_t)) equals RN_bf16(a s_t) unless the fp32 product lands
+      // exactly on a bf16 midpoint (low half 0x8000): only such lanes take the
+      // exact residual path.
+      float pr[8];
+      bool mid = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = nan ? 0x7FC00000u : as_u(a[i] * st);
-      } else {
-        // RN_bf16(RN_f32(a s_t)) equals RN_bf16(a s_t) unless the fp32 product lands
-        // exactly on a bf16 midpoint (low half 0x8000): only such lanes take the
-        // exact residual path.
-        float pr[8];
-        bool mid = false;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = a[i] * st;
-          mid |= (uint16_t)as_u(pr[i]) == 0x8000u;
-        }
-        uint32_t o[4];
-        if (!mid) {
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const bf16x2_t r = {(__bf16)pr[2 * h], (__bf16)pr[2 * h + 1]};
-            o[h] = __builtin_bit_cast(uint32_t, r);
-          }
-        } else {
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-            o[h] = bf16_of_product(a[2 * h], st_s, k) | (bf16_of_product(a[2 * h + 1], st_s, k) << 16);
-        }
-        const uint4 ov = nan ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u)
-                             : make_uint4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<uint4*>(p.y)[c] = ov;
-        continue;
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = a[i] * st;
+        mid |= (uint16_t)as_u(pr[i]) == 0x8000u;
       }
+      uint32_t o[4];
+      if (!mid) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const bf16x2_t r = {(__bf16)pr[2 * h], (__bf16)pr[2 * h + 1]};
+          o[h] = __builtin_bit_cast(uint32_t, r);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          o[h] = bf16_of_product(a[2 * h], st_s, k) | (bf16_of_product(a[2 * h + 1], st_s, k) << 16);
+      }
+      ov = nan ? make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u) : make_uint4(o[0], o[1], o[2], o[3]);
     }
-    if constexpr (OUT_F32) {
-      float4* y = reinterpret_cast<float4*>(p.y) + (size_t)c * 2;
-      y[0] = make_float4(as_f(out[0]), as_f(out[1]), as_f(out[2]), as_f(out[3]));
-      y[1] = make_float4(as_f(out[4]), as_f(out[5]), as_f(out[6]), as_f(out[7]));
+    store_nt(reinterpret_cast<uint4*>(p.y) + c, ov);
+  }
+}
+
+// fp32 output. A unit is 4 elements: 2 code bytes in, 16 bytes out. Consecutive
+// lanes take consecutive units, so every store instruction writes 1 KiB of whole
+// lines (a lane owning 8 elements would write its 32 bytes as two half-lines).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void dequant_f32_kernel(DeqParams p) {
+  constexpr int kU = 2 * kUnroll;
+  const uint32_t units = p.chunks * 2u;
+  const uint32_t base = blockIdx.x * (kThreads * kU) + threadIdx.x;
+  const uint16_t* codes = reinterpret_cast<const uint16_t*>(p.codes);
+  float st = 0.0f;
+  if constexpr (FMT == kNV) st = *p.tensor_scale;
+  uint32_t w[kU];
+  uint32_t sb[kU];
+#pragma unroll
+  for (int j = 0; j < kU; ++j) {
+    const uint32_t u = base + j * kThreads;
+    w[j] = 0;
+    sb[j] = 0;
+    if (u < units) {
+      w[j] = codes[u];
+      sb[j] = p.scales[FMT == kMX ? (u >> 3) : (u >> 2)];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kU; ++j) {
+    const uint32_t u = base + j * kThreads;
+    if (u >= units) continue;
+    float v[4];
+    bool nan;
+    if constexpr (FMT == kMX) {
+      const uint32_t byte = sb[j];
+      const float scale = e8m0_operand(min(byte, 254u));
+      nan = byte == 255u;
+      const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 0);
+      const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], scale, 1);
+      v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
     } else {
-      uint4 o = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16), out[4] | (out[5] << 16),
-                           out[6] | (out[7] << 16));
-      reinterpret_cast<uint4*>(p.y)[c] = o;
+      const uint32_t byte = sb[j];
+      nan = (byte & 0x7Fu) == 0x7Fu || !(fabsf(st) <= 3.40282347e38f);
+      const float sbv = as_f(as_u(e4m3_value(byte & 0x7Fu)) | ((byte & 0x80u) << 24));
+      const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 0);
+      const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[j], 1.0f, 1);
+      // v * s_b is exact (at most 6 significant bits); one rounding with s_t
+      v[0] = (a.x * sbv) * st; v[1] = (a.y * sbv) * st; v[2] = (b.x * sbv) * st; v[3] = (b.y * sbv) * st;
     }
+    const float qn = as_f(0x7FC00000u);
+    store_nt(reinterpret_cast<float4*>(p.y) + u,
+             nan ? make_float4(qn, qn, qn, qn) : make_float4(v[0], v[1], v[2], v[3]));
   }
 }
 
@@ -303,12 +325,13 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fm
     p.tensor_scale = tensor_scale;
     p.y = reinterpret_cast<uint8_t*>(y) + (size_t)r0 * cols * osz;
     const uint32_t grid = (p.chunks + kChunksPerWG - 1) / kChunksPerWG;
+    // both kernels cover kChunksPerWG chunks (8 elements each) per workgroup
     if (fmt == kMX) {
-      if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kMX, false>), dim3(grid), dim3(kThreads), 0, st, p);
-      else hipLaunchKernelGGL((dequant_kernel<kMX, true>), dim3(grid), dim3(kThreads), 0, st, p);
+      if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kMX>), dim3(grid), dim3(kThreads), 0, st, p);
+      else hipLaunchKernelGGL((dequant_f32_kernel<kMX>), dim3(grid), dim3(kThreads), 0, st, p);
     } else {
-      if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kNV, false>), dim3(grid), dim3(kThreads), 0, st, p);
-      else hipLaunchKernelGGL((dequant_kernel<kNV, true>), dim3(grid), dim3(kThreads), 0, st, p);
+      if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kNV>), dim3(grid), dim3(kThreads), 0, st, p);
+      else hipLaunchKernelGGL((dequant_f32_kernel<kNV>), dim3(grid), dim3(kThreads), 0, st, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
