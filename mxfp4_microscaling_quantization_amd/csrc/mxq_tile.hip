@@ -1,18 +1,18 @@
 // Column-wise (and fused row + column) quantisation from one read of the input.
 //
-// A 256-thread workgroup owns a 128 x 128 tile (64 x 128 for fp32 input, so the
-// LDS tile is 32 KB either way). Phase 1: every thread loads 16-byte chunks (a wave
-// reads four 256-byte row segments per instruction), quantises them row-wise if
-// asked (blocks along the row span a DPP quad, exactly as in the row kernel) and
-// parks the raw values in LDS. Phase 2: a task is one column over 32 rows; the
-// 32-row groups of a column sit on neighbouring lanes, so each store instruction
-// writes 64 contiguous bytes (16 bytes per lane) for each of 16 columns. The LDS
-// tile is XOR-swizzled so that phase 2 reads hit all 32 banks, and the optional
-// Hadamard transform runs along the rows in registers.
+// A 256-thread workgroup owns one tile (shape per variant, see TileShape; 32 KB of
+// LDS, 64 KB for the fused MXFP4 tile). Phase 1: every thread loads 16-byte chunks
+// (a wave reads whole 256- or 512-byte row segments per instruction), quantises
+// them row-wise if asked (blocks along the row span a DPP quad, exactly as in the
+// row kernel) and parks the raw values in LDS. Phase 2: a task is one column over
+// 32 rows; the 32-row groups of a column sit on neighbouring lanes, so each store
+// instruction writes a contiguous run of 16 bytes per group for each of its
+// columns. The LDS tile is XOR-swizzled so that phase 2 reads hit all 32 banks,
+// and the optional Hadamard transform runs along the rows in registers.
 //
-// Workgroups are dealt to the eight XCDs in turn; pairs of vertically adjacent
-// tiles go to one XCD in consecutive turns, so both halves of a 128-byte line of
-// column codes are written through the same L2.
+// Workgroups are dealt to the eight XCDs in turn; vertically adjacent tiles go to
+// one XCD in consecutive turns, so the pieces of a 128-byte line of column codes
+// are written through the same L2.
 #include <algorithm>
 
 #include "mxq_blocks.h"
@@ -21,14 +21,21 @@
 namespace mxq {
 
 constexpr int kTileThreads = 256;
-// Tile shape per input type.
-template <typename T>
+// Tile shape per variant, as measured on inputs read from HBM: 128 x 128 for the
+// column-only and the NVFP4 kernels; the fused row + column MXFP4 kernels use 256
+// columns, so each row's codes leave as a whole 128-byte line (128 rows, or 64 with
+// the Hadamard transform, whose heavier register use favours the smaller tile).
+// fp32 tiles have half the rows. V vertically adjacent tiles (256 rows of bf16) are
+// dealt to the same XCD in consecutive turns.
+template <typename T, int FMT, bool RHT, bool ROW>
 struct TileShape {
-  static constexpr int R = sizeof(T) == 2 ? 128 : 64;
-  static constexpr int C = 128;     // a multiple of 64
-  static constexpr int G = R / 32;  // 32-row groups of a column
+  static constexpr bool kWide = ROW && FMT == kMX;
+  static constexpr int C = kWide ? 256 : 128;                // a multiple of 64
+  static constexpr int R16 = kWide && RHT ? 64 : 128;        // rows for bf16 input
+  static constexpr int R = sizeof(T) == 2 ? R16 : R16 / 2;  // at least 32
+  static constexpr int G = R / 32;                           // 32-row groups of a column
+  static constexpr int V = 256 / R16;
 };
-constexpr int kVGroup = 2;  // vertically adjacent tiles dispatched together
 
 struct TileParams {
   const void* x;
@@ -139,7 +146,8 @@ __device__ __forceinline__ int swz(int r, int c) {
 template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
 __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams p) {
   // LDS tile of raw input values, row-major [128][128], XOR-swizzled columns
-  constexpr int kTileR = TileShape<T>::R, kTileC = TileShape<T>::C, kRowGroups = TileShape<T>::G;
+  using Shape = TileShape<T, FMT, RHT, ROW>;
+  constexpr int kTileR = Shape::R, kTileC = Shape::C, kRowGroups = Shape::G, kVGroup = Shape::V;
   __shared__ T tile[kTileR][kTileC];
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t t = threadIdx.x;
@@ -255,9 +263,10 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   }
 }
 
-template <typename T, int FMT, bool SR, bool RHT>
-static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
-  constexpr int kTileR = TileShape<T>::R, kTileC = TileShape<T>::C;
+template <typename T, int FMT, bool SR, bool RHT, bool ROW>
+static hipError_t launch_tiles_shape(const TileLaunch& a, hipStream_t st) {
+  using Shape = TileShape<T, FMT, RHT, ROW>;
+  constexpr int kTileR = Shape::R, kTileC = Shape::C, kVGroup = Shape::V;
   // slabs of at most 2^22 tiles (cols <= 2^30 gives at most 2^23 tiles per tile row)
   const int64_t tiles_per_row = (a.cols + kTileC - 1) / kTileC;
   const int64_t max_rows = (int64_t)kTileR * std::max<int64_t>(1, ((int64_t)1 << 22) / tiles_per_row);
@@ -289,16 +298,17 @@ static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
     p.amax = a.amax;
     p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
     const uint32_t grid = 8u * kVGroup * ((p.groups + 7u) / 8u);
-    if (a.want_row && a.want_col)
-      hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, true, true>), dim3(grid),
-                         dim3(kTileThreads), 0, st, p);
-    else
-      hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, false, true>), dim3(grid),
-                         dim3(kTileThreads), 0, st, p);
+    hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, ROW, true>), dim3(grid), dim3(kTileThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <typename T, int FMT, bool SR, bool RHT>
+static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
+  return a.want_row ? launch_tiles_shape<T, FMT, SR, RHT, true>(a, st)
+                    : launch_tiles_shape<T, FMT, SR, RHT, false>(a, st);
 }
 
 template <typename T, int FMT>
