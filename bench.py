@@ -185,6 +185,7 @@ def config_report(dev, reps: int = 30) -> list:
     out = []
 
     def row(cfg, name, fn, n, nbytes, elems):
+        warm()
         us = timed(fn, n)
         r = {"config": cfg, "kernel": name, "us": round(us, 3), "bytes": nbytes, "GB_s": round(nbytes / us / 1e3, 1),
              "elements_per_s": round(elems / (us * 1e-6), 1), "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -195,13 +196,15 @@ def config_report(dev, reps: int = 30) -> list:
     def copies(t, n):
         return [t.to(dev) for _ in range(n)]
 
-    # warm the clocks up
+    # the inputs are generated on the host while the GPU idles: bring its clocks up
+    # again before each configuration is timed
     w = workloads.mxfp4_rowwise_moe().x.to(dev)
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.3:
-        mxq.mxq_quantize(w, "mxfp4", "row", "sr", sr_seed=1)
-        torch.cuda.synchronize()
-    del w
+
+    def warm():
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            mxq.mxq_quantize(w, "mxfp4", "row", "sr", sr_seed=1)
+            torch.cuda.synchronize()
     for cfg, n, wl in ((1, 64, workloads.mxfp4_rowwise_small()), (2, 3, workloads.mxfp4_rowwise_moe())):
         xs = copies(wl.x, n)
         R, C = wl.x.shape
@@ -245,6 +248,7 @@ def config_report(dev, reps: int = 30) -> list:
     row(5, "nvfp4_quantize_rne", lambda k: mxq.mxq_quantize(xs[k], "nvfp4", "row", amax=amax[k], out=os_[k]), n, b, N)
     row(5, "nvfp4_quantize_sr", lambda k: mxq.mxq_quantize(xs[k], "nvfp4", "row", "sr", sr_seed=wl.sr_seed,
                                                             amax=amax[k], out=os_[k]), n, b, N)
+    del w
     return out
 
 

@@ -421,20 +421,25 @@ __device__ __forceinline__ uint32_t nv_codes8_rne(const float* v, const NvTensor
   const uint32_t chi = fp4x8_from_f32(yhi, 1.0f);
   const uint32_t diff = clo ^ chi;
   if (diff == 0u) return clo;
-  // some element lies within 2^-20 of a midpoint: decide exactly the ones that do
+  // Some element lies within 2^-20 of a midpoint: decide exactly the ones that do,
+  // one per iteration (usually one; such elements are rare but can be structural,
+  // e.g. bf16 data whose exact quotients hit midpoints up to the rounding of s_t).
   uint32_t out = clo;
+  uint32_t pending = diff;
+  while (pending) {
+    const uint32_t sh = (uint32_t)__builtin_ctz(pending) & ~3u;  // bit offset of the nibble
+    pending &= ~(0xFu << sh);
+    const uint32_t lo = (clo >> sh) & 0xFu, hi = (chi >> sh) & 0xFu;
+    float xv = v[0];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if ((diff >> (4 * i)) & 0xFu) {
-      const uint32_t lo = (clo >> (4 * i)) & 0xFu, hi = (chi >> (4 * i)) & 0xFu;
-      // the two neighbouring grid values, decoded together: m is their midpoint
-      const f32x2_t g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((lo & 7u) | ((hi & 7u) << 4), 1.0f, 0);
-      const float m = 0.5f * (g.x + g.y);
-      const float xs = fast ? fabsf(v[i]) : ldexpf(fabsf(v[i]), -t.et);
-      const float d = fmaf(m * sb, sts, -xs);  // > 0: the quotient is below m
-      const uint32_t c = d > 0.0f ? lo : (d < 0.0f ? hi : ((lo & 1u) ? hi : lo));
-      out = (out & ~(0xFu << (4 * i))) | (c << (4 * i));
-    }
+    for (int j = 1; j < 8; ++j) xv = sh == 4u * j ? v[j] : xv;
+    // the two neighbouring grid values, decoded together: m is their midpoint
+    const f32x2_t g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((lo & 7u) | ((hi & 7u) << 4), 1.0f, 0);
+    const float m = 0.5f * (g.x + g.y);
+    const float xs = fast ? fabsf(xv) : ldexpf(fabsf(xv), -t.et);
+    const float d = fmaf(m * sb, sts, -xs);  // > 0: the quotient is below m
+    const uint32_t c = d > 0.0f ? lo : (d < 0.0f ? hi : ((lo & 1u) ? hi : lo));
+    out = (out & ~(0xFu << sh)) | (c << sh);
   }
   return out;
 }
