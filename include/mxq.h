@@ -159,7 +159,12 @@ mxq_status mxq_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* e8m0, int64_t r
  * sign_mask is set (sign_mask 0 = deterministic H16). y is computed in fp32
  * (butterfly stages 1, 2, 4, 8, then the exact scaling by 1/4) and quantised
  * without an intermediate bf16 rounding. Arguments otherwise as mxq_quantize;
- * MXFP4 only. rows % 32 == 0 when a column-wise output is requested.
+ * rows % 32 (MXFP4) or % 16 (NVFP4) == 0 when a column-wise output is requested.
+ * NVFP4 (the pages' wgrad recipe): the tensor scale belongs to the transformed
+ * tensor, so amax must be the amax of y along the requested axis (mxq_rht_amax);
+ * the row- and column-wise transforms have different amaxes, so axis must be
+ * MXQ_ROWWISE or MXQ_COLWISE (MXQ_BOTH returns MXQ_EUNSUPPORTED). tensor_scale
+ * receives s_t of y.
  */
 mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                             mxq_format fmt, mxq_axis axis, uint32_t sign_mask, mxq_round rnd,
@@ -173,6 +178,17 @@ mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t c
  */
 mxq_status mxq_rht_apply(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                          uint32_t sign_mask, float* y, void* stream);
+
+/*
+ * mxq_rht_amax - the tensor amax of the transformed tensor, max |y| with
+ * y = (1/4) H16 (s * x) taken along the rows (axis MXQ_ROWWISE, cols % 16 == 0) or
+ * along the columns (MXQ_COLWISE, rows % 16 == 0, cols % 8 == 0), computed as
+ * mxq_rht_quantize computes y (fp32 butterfly). This is the amax NVFP4 with the
+ * Hadamard transform takes ([NVFP4] section 2B). Writes fp32 amax_out[0] (device);
+ * NaN/Inf propagate as in mxq_amax; rows == 0 writes 0. MXQ_BOTH: MXQ_EINVAL.
+ */
+mxq_status mxq_rht_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                        mxq_axis axis, uint32_t sign_mask, float* amax_out, void* stream);
 
 /*
  * mxq_amax - the tensor amax max|x| that NVFP4's tensor scale needs ([NVFP4]

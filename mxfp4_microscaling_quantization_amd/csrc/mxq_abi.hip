@@ -142,7 +142,10 @@ mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t c
                             uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
                             uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                             const float* amax, float* tensor_scale, void* stream) {
-  if (fmt != MXQ_MXFP4) return fmt == MXQ_NVFP4 ? MXQ_EUNSUPPORTED : MXQ_EINVAL;
+  if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4) return MXQ_EINVAL;
+  // NVFP4 takes one tensor scale per call, from the amax of the transform along the
+  // block axis; the row- and column-wise transforms differ, so one axis per call
+  if (fmt == MXQ_NVFP4 && axis == MXQ_BOTH) return MXQ_EUNSUPPORTED;
   return quantize_impl(x, dt, rows, cols, ldx, fmt, axis, true, sign_mask, rnd, sr_seed, sr_offset,
                        codes_row, scales_row, codes_col, scales_col, amax, tensor_scale, stream);
 }
@@ -216,6 +219,24 @@ mxq_status mxq_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int
   const int64_t esz = dt == MXQ_BF16 ? 2 : 4;
   if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(amax_out, 4)) return MXQ_EALIGN;
   return from_hip(launch_amax(x, dt, rows, cols, ldx, amax_out, st));
+}
+
+mxq_status mxq_rht_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                        mxq_axis axis, uint32_t sign_mask, float* amax_out, void* stream) {
+  if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;
+  if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE) return MXQ_EINVAL;
+  if (rows < 0 || cols < 0) return MXQ_EINVAL;
+  if (!amax_out) return MXQ_EINVAL;
+  const bool colwise = axis == MXQ_COLWISE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (rows == 0) return from_hip(launch_rht_amax(x, dt, 0, cols, ldx, colwise, 0, amax_out, st));
+  if (!x) return MXQ_EINVAL;
+  if (cols == 0 || ldx < cols) return MXQ_ESHAPE;
+  if (colwise ? (rows % 16 || cols % 8) : (cols % 16 != 0)) return MXQ_ESHAPE;
+  if (too_large(rows, cols)) return MXQ_ESHAPE;
+  const int64_t esz = dt == MXQ_BF16 ? 2 : 4;
+  if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(amax_out, 4)) return MXQ_EALIGN;
+  return from_hip(launch_rht_amax(x, dt, rows, cols, ldx, colwise, sign_mask & 0xFFFFu, amax_out, st));
 }
 
 uint32_t mxq_rht_signs(uint64_t seed) { return philox_word0(0, seed) & 0xFFFFu; }

@@ -41,6 +41,17 @@ __device__ __forceinline__ void zero_raw(Raw<float>& r) {
   r.b = r.a;
 }
 
+// Element j (0..7) of a chunk as fp32.
+__device__ __forceinline__ float raw_elem(const Raw<uint16_t>& r, int j) {
+  const uint32_t w = j < 2 ? r.w.x : (j < 4 ? r.w.y : (j < 6 ? r.w.z : r.w.w));
+  return as_f((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+__device__ __forceinline__ float raw_elem(const Raw<float>& r, int j) {
+  const float4& q = j < 4 ? r.a : r.b;
+  const int k = j & 3;
+  return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w));
+}
+
 __device__ __forceinline__ void to_f32(const Raw<uint16_t>& r, float v[8]) {
   const uint32_t w[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
 #pragma unroll
@@ -108,6 +119,23 @@ __device__ __forceinline__ void h16_pair(float v[8], uint32_t half) {
     v[i] = o + as_f(as_u(v[i]) ^ neg);
   }
 }
+
+// In-thread Hadamard of 16 values (signs already applied): stages 1, 2, 4, 8 in
+// fp32; the factor 1/4 is folded into the block scale by the caller.
+__device__ __forceinline__ void h16_local(float* v) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
 
 // NaN-propagating max of |v| over 8 values (v_maximum3_f32 with abs modifiers).
 __device__ __forceinline__ float absmax8(const float* v) {

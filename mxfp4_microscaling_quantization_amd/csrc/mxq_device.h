@@ -303,6 +303,16 @@ struct NvTensor {
   int et;
 };
 
+// With the Hadamard transform the kernels quantise z = H16 (s * x), four times the
+// transformed values y = z / 4 whose amax sets s_t: quantising z against 4 s_t
+// (exact) gives the same block scales and codes as y against s_t.
+__device__ __forceinline__ void nv_tensor_times4(NvTensor& t) {
+  if (t.mode == 0) {
+    t.st *= 4.0f;
+    t.et += 2;
+  }
+}
+
 __device__ __forceinline__ NvTensor nv_tensor(float amax) {
   NvTensor t;
   const float a = fabsf(amax);

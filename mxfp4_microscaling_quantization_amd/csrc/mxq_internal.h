@@ -69,6 +69,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fm
 hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                        float* amax_out, hipStream_t st);
 
+hipError_t launch_rht_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, bool colwise,
+                           uint32_t sign_mask, float* amax_out, hipStream_t st);
 hipError_t launch_rht_apply(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                             uint32_t sign_mask, float* y, hipStream_t st);
 

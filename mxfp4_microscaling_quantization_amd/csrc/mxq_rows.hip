@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
   if constexpr (FMT == kNV) {
     nt = nv_tensor(*p.amax);
     if (p.tensor_scale && blockIdx.x == 0 && threadIdx.x == 0) *p.tensor_scale = nt.st;
+    if constexpr (RHT) nv_tensor_times4(nt);
   }
   // a chunk's parity (its half of a 16-element Hadamard chunk) is the lane's parity
   SignFlips flips;
@@ -421,6 +422,148 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
   }
   return hipSuccess;
 }
+
+// Amax of the Hadamard transform: max |(1/4) H16 (s * x)| over every 16-chunk along
+// the rows (the tensor amax for NVFP4 quantisation of the transformed tensor). The
+// factor 1/4 is exact and applied to each thread's maximum.
+template <typename T, bool CONTIG>
+__global__ __launch_bounds__(kThreads) void rht_amax_rows_kernel(RowParams p, uint32_t* out) {
+  const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  // a chunk's parity (its half of a 16-element chunk) is the lane's parity: the
+  // grid stride is even, and so is the chunk count (cols % 16 == 0), so the two lanes
+  // of a pair always leave the loop together
+  const SignFlips flips = make_flips<T>(p.sign_mask, threadIdx.x & 1u);
+  float m = 0.0f;
+  constexpr int U = 4;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t c0 = blockIdx.x * kThreads + threadIdx.x; c0 < p.chunks; c0 += stride * U) {
+    Raw<T> r[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t c = c0 + j * stride;
+      if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), r[j]);
+      else zero_raw(r[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      flip(r[j], flips);
+      float v[8];
+      to_f32(r[j], v);
+      h16_pair(v, threadIdx.x & 1u);
+      m = __builtin_elementwise_maximum(m, absmax8(v));
+    }
+  }
+  uint32_t mb = as_u(m * 0.25f) & 0x7FFFFFFFu;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mb;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) v = max(v, red[i]);
+    atomicMax(out, v);
+  }
+}
+
+// The same along the columns: a unit is 16 rows x 8 columns; the transform runs down
+// each column in registers (row i of the unit takes sign bit i).
+struct RhtColParams {
+  const void* x;
+  int64_t ldx;
+  uint32_t cpr;    // 8-column chunks per row
+  uint32_t units;  // (rows / 16) * cpr
+  uint32_t sign_mask;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rht_amax_cols_kernel(RhtColParams p, uint32_t* out) {
+  const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
+  float m = 0.0f;
+  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < p.units; u += gridDim.x * kThreads) {
+    const uint32_t g = u / p.cpr, c = u - g * p.cpr;
+    Raw<T> r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) load_raw(x, (size_t)(16 * g + i) * p.ldx + (size_t)c * 8, r[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = raw_elem(r[i], j);
+        v[i] = ((p.sign_mask >> i) & 1u) ? -e : e;
+      }
+      h16_local(v);
+      m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(absmax8(v), absmax8(v + 8)));
+    }
+  }
+  uint32_t mb = as_u(m * 0.25f) & 0x7FFFFFFFu;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mb;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) v = max(v, red[i]);
+    atomicMax(out, v);
+  }
+}
+
+hipError_t launch_rht_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, bool colwise,
+                           uint32_t sign_mask, float* amax_out, hipStream_t st) {
+  hipLaunchKernelGGL(amax_init_kernel, dim3(1), dim3(1), 0, st, amax_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows == 0) return e;
+  const size_t esz = dtype == 0 ? 2 : 4;
+  uint32_t* out = reinterpret_cast<uint32_t*>(amax_out);
+  const int64_t cpr = cols / 8;
+  if (!colwise) {
+    const int64_t max_rows = std::max<int64_t>(1, ((int64_t)1 << 30) / cpr);
+    for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+      const int64_t nr = std::min(max_rows, rows - r0);
+      RowParams p{};
+      p.x = reinterpret_cast<const uint8_t*>(x) + (size_t)r0 * ldx * esz;
+      p.ldx = ldx;
+      p.chunks = (uint32_t)(nr * cpr);
+      FastDivHost fd = make_fastdiv((uint32_t)cpr);
+      p.cpr = FastDiv{fd.d, fd.m, fd.s};
+      p.sign_mask = sign_mask;
+      const uint32_t want = (p.chunks + kThreads * 4 - 1) / (kThreads * 4);
+      const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 512));
+      const bool contig = ldx == cols;
+      if (dtype == 0) {
+        if (contig) hipLaunchKernelGGL((rht_amax_rows_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, st, p, out);
+        else hipLaunchKernelGGL((rht_amax_rows_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, st, p, out);
+      } else {
+        if (contig) hipLaunchKernelGGL((rht_amax_rows_kernel<float, true>), dim3(grid), dim3(kThreads), 0, st, p, out);
+        else hipLaunchKernelGGL((rht_amax_rows_kernel<float, false>), dim3(grid), dim3(kThreads), 0, st, p, out);
+      }
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  // column direction: slabs of whole 16-row groups with fewer than 2^30 units
+  const int64_t max_rows = 16 * std::max<int64_t>(1, ((int64_t)1 << 30) / cpr);
+  for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, rows - r0);
+    RhtColParams p;
+    p.x = reinterpret_cast<const uint8_t*>(x) + (size_t)r0 * ldx * esz;
+    p.ldx = ldx;
+    p.cpr = (uint32_t)cpr;
+    p.units = (uint32_t)((nr / 16) * cpr);
+    p.sign_mask = sign_mask;
+    const uint32_t want = (p.units + kThreads - 1) / kThreads;
+    const uint32_t grid = std::max<uint32_t>(1, std::min<uint32_t>(want, 1024));
+    if (dtype == 0) hipLaunchKernelGGL((rht_amax_cols_kernel<uint16_t>), dim3(grid), dim3(kThreads), 0, st, p, out);
+    else hipLaunchKernelGGL((rht_amax_cols_kernel<float>), dim3(grid), dim3(kThreads), 0, st, p, out);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 
 // ---------------------------------------------------------------------------
 // The transform alone, fp32 out.

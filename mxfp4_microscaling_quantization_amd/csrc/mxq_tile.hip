@@ -53,22 +53,6 @@ struct TileParams {
   float* tensor_scale;
 };
 
-// In-thread Hadamard of 16 values (signs already applied): stages 1, 2, 4, 8 in
-// fp32; the factor 1/4 is folded into the block scale by the caller.
-__device__ __forceinline__ void h16_local(float* v) {
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-}
-
 __device__ __forceinline__ float absmax32(const float* v) {
   float m = __builtin_elementwise_maximum(__builtin_fabsf(v[0]), __builtin_fabsf(v[1]));
 #pragma unroll
@@ -155,6 +139,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   if constexpr (FMT == kNV) {
     nt = nv_tensor(*p.amax);
     if (p.tensor_scale && blockIdx.x == 0 && t == 0) *p.tensor_scale = nt.st;
+    if constexpr (RHT) nv_tensor_times4(nt);
   }
   SignFlips flips;
   if constexpr (RHT && ROW) flips = make_flips<T>(p.sign_mask, t & 1u);

@@ -48,12 +48,13 @@ def lib() -> ctypes.CDLL:
     L.mxq_mxfp4_to_fp8.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.mxq_rht_apply.argtypes = [vp, i32, i64, i64, i64, u32, vp, vp]
     L.mxq_amax.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    L.mxq_rht_amax.argtypes = [vp, i32, i64, i64, i64, i32, u32, vp, vp]
     L.mxq_rht_signs.argtypes = [u64]
     L.mxq_rht_signs.restype = u32
     L.mxq_status_string.argtypes = [i32]
     L.mxq_status_string.restype = ctypes.c_char_p
     for name in ("mxq_quantize", "mxq_rht_quantize", "mxq_dequantize", "mxq_fp8_to_mxfp4",
-                 "mxq_mxfp4_to_fp8", "mxq_rht_apply", "mxq_amax"):
+                 "mxq_mxfp4_to_fp8", "mxq_rht_apply", "mxq_amax", "mxq_rht_amax"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -193,4 +194,15 @@ def mxq_amax(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tenso
     rows, cols, ldx = _rows_view(x)
     a = out if out is not None else torch.empty((1,), dtype=torch.float32, device=x.device)
     _check(lib().mxq_amax(_ptr(x), _dtype_code(x), rows, cols, ldx, _ptr(a), _stream()))
+    return a
+
+
+def mxq_rht_amax(x: torch.Tensor, sign_mask: int, axis: str = "row",
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mxq_rht_amax: max |(1/4) H16 (s * x)| with the transform along rows ("row") or
+    columns ("col"), as a device fp32[1]."""
+    rows, cols, ldx = _rows_view(x)
+    a = out if out is not None else torch.empty((1,), dtype=torch.float32, device=x.device)
+    _check(lib().mxq_rht_amax(_ptr(x), _dtype_code(x), rows, cols, ldx, _AXIS[axis], sign_mask, _ptr(a),
+                              _stream()))
     return a

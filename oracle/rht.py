@@ -19,12 +19,16 @@ Readings:
      rounding; this oracle computes y in float64 (the pages fix no precision).
   H4 row-wise: chunks along columns; column-wise: chunks along rows (the transform
      of x.T, then column-wise quantisation = row-wise quantisation of the transpose).
+  H5 NVFP4 with the transform (the weight-gradient recipe of [NVFP4] section 2B):
+     the two-level quantisation is applied to y, so the tensor scale comes from the
+     amax of y (the tensor that is quantised), taken along the quantisation axis.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .mx import mxfp4_quantize_rowwise
+from .nvfp4 import nvfp4_quantize_rowwise, tensor_amax
 from .philox import philox4x32_10
 
 RHT_N = 16
@@ -73,3 +77,19 @@ def rht_mxfp4_colwise(x: np.ndarray, mask: int):
     """Column-wise MXFP4 quantisation of the transform taken along rows (H4):
     row-wise quantisation of rht_rowwise(x.T)."""
     return mxfp4_quantize_rowwise(rht_rowwise(np.asarray(x, dtype=np.float64).T, mask))
+
+
+def rht_amax(x: np.ndarray, mask: int, axis: str = "row") -> float:
+    """H5: amax of the transform taken along rows ("row") or along columns ("col")."""
+    x = np.asarray(x, dtype=np.float64)
+    return tensor_amax(rht_rowwise(x if axis == "row" else x.T, mask))
+
+
+def rht_nvfp4_rowwise(x: np.ndarray, mask: int, amax: float | None = None, r16=None):
+    """H5: row-wise NVFP4 of the row-wise transform (amax defaults to the transform's)."""
+    return nvfp4_quantize_rowwise(rht_rowwise(x, mask), amax=amax, r16=r16)
+
+
+def rht_nvfp4_colwise(x: np.ndarray, mask: int, amax: float | None = None, r16_t=None):
+    """H5: column-wise NVFP4 of the transform along rows of x.T (H4)."""
+    return nvfp4_quantize_rowwise(rht_rowwise(np.asarray(x, dtype=np.float64).T, mask), amax=amax, r16=r16_t)

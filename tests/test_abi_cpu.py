@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     L = mxq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -84,8 +84,13 @@ def test_other_entry_points_validation():
     assert L.mxq_mxfp4_to_fp8(FAKE, FAKE + 1, 4, 128, FAKE, FAKE, None) == mxq.MXQ_EALIGN
     assert L.mxq_mxfp4_to_fp8(FAKE, FAKE, 0, 128, FAKE, FAKE, None) == mxq.MXQ_OK
     assert L.mxq_rht_apply(FAKE, 0, 4, 40, 40, 0, FAKE, None) == mxq.MXQ_ESHAPE
-    assert L.mxq_rht_quantize(FAKE, 0, 4, 64, 64, 1, 1, 0, 0, 0, 0, FAKE, FAKE, None, None, FAKE, FAKE,
+    # NVFP4 with the transform: one axis per call
+    assert L.mxq_rht_quantize(FAKE, 0, 32, 64, 64, 1, 3, 0, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               None) == mxq.MXQ_EUNSUPPORTED
+    assert L.mxq_rht_amax(FAKE, 0, 32, 64, 64, 3, 0, FAKE, None) == mxq.MXQ_EINVAL
+    assert L.mxq_rht_amax(FAKE, 0, 32, 40, 40, 1, 0, FAKE, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_rht_amax(FAKE, 0, 24, 64, 64, 2, 0, FAKE, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_rht_amax(FAKE, 0, 32, 64, 64, 1, 0, None, None) == mxq.MXQ_EINVAL
     assert L.mxq_amax(FAKE, 0, 4, 64, 64, None, None) == mxq.MXQ_EINVAL
     assert L.mxq_amax(FAKE, 0, 1, 2 ** 31, 2 ** 31, FAKE, None) == mxq.MXQ_ESHAPE
     assert L.mxq_dequantize(FAKE, FAKE, 0, 1, 2 ** 31, None, FAKE, 0, None) == mxq.MXQ_ESHAPE
