@@ -23,6 +23,12 @@ Readings (the pages give no formulas):
      of the exact product).
   N5 column-wise NVFP4 (blocks of 16 along rows) is the row-wise quantisation of
      the transpose with the same tensor scale.
+  N6 2D scaling for weights ([NVFP4] section 2B.3, 16x16 blocks): one block scale
+     per 16x16 tile, s_b = RNE_E4M3(a_b / (6 * s_t)) with a_b = max |x| over the 256
+     elements, codes as in N3 with that scale. The result is stored in the 1x16
+     layout (each tile's scale repeated on its 16 rows), so the transpose's
+     quantisation is exactly the transpose of the codes and of the scales: the
+     same quantised weights serve both passes. Round to nearest even only.
 
 Why float64 decides every rounding here exactly: each rounding compares an exact
 quotient a/b (a at most 24 significant bits, b at most 28) with a threshold of at
@@ -125,3 +131,36 @@ def nvfp4_dequantize(packed: np.ndarray, sb_bytes: np.ndarray, st: float, out_dt
         bits[np.isnan(v)] = 0x7FC00000
         return bits
     raise ValueError(out_dtype)
+
+
+def nvfp4_quantize_2d(x: np.ndarray, amax: float | None = None):
+    """N6: NVFP4 with 16x16 block scales of a real [R, C] matrix (R, C % 16 == 0).
+
+    Returns (codes uint8 [R, C/2], E4M3 scales uint8 [R, C/16] in the 1x16 layout
+    (equal within each 16-row group), s_t float32)."""
+    x = np.asarray(x, dtype=np.float64)
+    R, C = x.shape
+    if R % NV_BLOCK or C % NV_BLOCK:
+        raise ValueError("rows and columns must be multiples of 16")
+    A = tensor_amax(x) if amax is None else float(amax)
+    st = tensor_scale(A)
+    if np.isnan(st):
+        return (np.zeros((R, C // 2), np.uint8), np.full((R, C // NV_BLOCK), 0x7F, np.uint8), st)
+    sign = (np.signbit(x).astype(np.uint8) << 3)
+    if st == 0:
+        return (pack_nibbles(sign), np.zeros((R, C // NV_BLOCK), np.uint8), st)
+    st64 = np.float64(st)
+    t = x.reshape(R // NV_BLOCK, NV_BLOCK, C // NV_BLOCK, NV_BLOCK)
+    finite = np.isfinite(t).all(axis=(1, 3))              # [R/16, C/16]
+    ab = np.abs(np.where(finite[:, None, :, None], t, 0.0)).max(axis=(1, 3))
+    sb_bytes = e4m3_round_nearest_even(ab / (6.0 * st64))  # N2 on the 16x16 amax
+    sb = e4m3_decode(sb_bytes)
+    denom = np.repeat(np.repeat(sb * st64, NV_BLOCK, axis=0), NV_BLOCK, axis=1)  # [R, C]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.abs(np.where(np.isfinite(x), x, 0.0)) / denom
+    y = np.where(denom > 0, y, 0.0)
+    mag = e2m1_encode_magnitude(y)
+    fin = np.repeat(np.repeat(finite, NV_BLOCK, axis=0), NV_BLOCK, axis=1)
+    codes = np.where(fin, mag | sign, 0).astype(np.uint8)
+    sb_bytes = np.where(finite, sb_bytes, np.uint8(0x7F)).astype(np.uint8)
+    return pack_nibbles(codes), np.repeat(sb_bytes, NV_BLOCK, axis=0), st

@@ -207,3 +207,50 @@ def test_stochastic_rounding_keeps_grid_values():
     p, sb, st = nvfp4.nvfp4_quantize_rowwise(x, r16=r16)
     p0, sb0, st0 = nvfp4.nvfp4_quantize_rowwise(x)
     np.testing.assert_array_equal(p, p0)
+
+
+def test_2d_equals_1d_when_every_row_block_holds_the_tile_maximum():
+    # when each 1x16 row block of a 16x16 tile reaches the tile's maximum, the 2D
+    # block amax equals every 1D block amax, so both quantisations coincide
+    rng = np.random.default_rng(4)
+    R, C = 48, 64
+    x = rng.standard_normal((R, C))
+    tmax = np.exp2(rng.integers(-3, 4, (R // 16, C // 16))) * 3.0
+    x = np.clip(x, -2.9, 2.9) * np.repeat(np.repeat(tmax / 3.0, 16, 0), 16, 1)
+    pos = rng.integers(0, 16, (R, C // 16))
+    for r in range(R):
+        for b in range(C // 16):
+            x[r, 16 * b + pos[r, b]] = tmax[r // 16, b] * (1 if (r + b) % 2 else -1)
+    c2, s2, st2 = nvfp4.nvfp4_quantize_2d(x)
+    c1, s1, st1 = nvfp4.nvfp4_quantize_rowwise(x)
+    assert st1 == st2
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_2d_transpose_symmetry_and_tile_constant_scales():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-3, 3, (64, 1)))
+    c, s, st = nvfp4.nvfp4_quantize_2d(x)
+    ct, stt, stt_t = nvfp4.nvfp4_quantize_2d(x.T)
+    assert st == stt_t
+    assert np.array_equal(mx.unpack_nibbles(ct), mx.unpack_nibbles(c).T)
+    # the scales are constant within a tile, and the transpose's are the transpose
+    tiles = s.reshape(4, 16, 6)
+    assert (tiles == tiles[:, :1, :]).all()
+    assert np.array_equal(stt[::16], s[::16].T)
+
+
+def test_2d_single_tile_by_hand():
+    # one 16x16 tile holding the tensor maximum A = 10.5, so s_t = A / 2688 = 2^-8 is
+    # exact and s_b = 448 (byte 0x7E); an element then codes as E2M1(6 |x| / A)
+    x = np.zeros((16, 16))
+    x[0, 0] = 10.5       # 6                      -> code 7
+    x[5, 7] = -5.25      # 3                      -> code 5, negative
+    x[9, 3] = 2.625      # 1.5                    -> code 3
+    x[15, 15] = 1.3125   # 0.75, a tie of 0.5 and 1 -> even: 1.0, code 2
+    x[2, 2] = 0.4375     # 0.25, a tie of 0 and 0.5 -> even: 0, code 0
+    c, s, st = nvfp4.nvfp4_quantize_2d(x)
+    assert st == np.float32(2.0 ** -8) and (s == 0x7E).all()
+    g = mx.unpack_nibbles(c)
+    assert g[0, 0] == 7 and g[5, 7] == 0x8 | 5 and g[9, 3] == 3 and g[15, 15] == 2 and g[2, 2] == 0
+    assert (np.delete(g.reshape(-1), [0, 5 * 16 + 7, 9 * 16 + 3, 255]) == 0).all()
