@@ -66,7 +66,7 @@ typedef enum {
 } mxq_status;
 
 typedef enum { MXQ_BF16 = 0, MXQ_F32 = 1 } mxq_dtype;
-typedef enum { MXQ_MXFP4 = 0, MXQ_NVFP4 = 1 } mxq_format;
+typedef enum { MXQ_MXFP4 = 0, MXQ_NVFP4 = 1, MXQ_NVFP4_2D = 2 } mxq_format;
 typedef enum { MXQ_RNE = 0, MXQ_SR = 1 } mxq_round;
 typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
 
@@ -84,6 +84,13 @@ typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
  *   sign | E2M1 rounding of the exact quotient |x| / (s_b s_t). s_t == 0 gives
  *   scale bytes 0 and sign-only codes, a block with s_b == 0 sign-only codes, a
  *   NaN/Inf amax (or a NaN/Inf block) scale bytes 0x7F and codes 0.
+ * NVFP4_2D ([NVFP4] section 2B, 16x16 blocks for weights): as NVFP4 but one block
+ *   scale per 16x16 tile (its max |x| over 256 elements), written in the NVFP4
+ *   layout with the tile's byte repeated on its 16 rows (row-wise) or columns
+ *   (column-wise): the column-wise output is exactly the transpose of the row-wise
+ *   one, so one quantisation serves W and W^T, and mxq_dequantize reads it as
+ *   NVFP4. rows % 16 == 0 and cols % 16 == 0 for any axis; round to nearest even
+ *   only (MXQ_SR returns MXQ_EUNSUPPORTED).
  * Stochastic rounding (rnd == MXQ_SR; [NVFP4] section 2B, gradients): element n
  *   (n = sr_offset + its row-major index in the tensor quantised; for column-wise
  *   outputs the index in the transpose) draws the 32-bit word n mod 4 of
@@ -96,8 +103,8 @@ typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
  * axis         MXQ_ROWWISE writes codes_row/scales_row, MXQ_COLWISE codes_col/
  *              scales_col, MXQ_BOTH both from a single read of x. Unused output
  *              pointers may be NULL.
- * amax         NVFP4 only: device fp32[1] holding the tensor amax (read only).
- * tensor_scale NVFP4 only: device fp32[1] receiving s_t (may be NULL).
+ * amax         NVFP4 / NVFP4_2D: device fp32[1] holding the tensor amax (read only).
+ * tensor_scale NVFP4 / NVFP4_2D: device fp32[1] receiving s_t (may be NULL).
  * Shapes: cols % bs == 0 for row-wise; rows % bs == 0 for column-wise outputs.
  */
 mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
@@ -114,7 +121,8 @@ mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
  * are always exact). MXFP4: scale = 2^(byte - 127). NVFP4: scale = E4M3(byte) *
  * (*tensor_scale). A NaN scale gives the quiet NaN 0x7FC0 / 0x7FC00000.
  * codes [rows, cols/2], scales [rows, cols/bs], y [rows, cols] of out_dt, dense.
- * tensor_scale: device fp32[1], NVFP4 only. cols % bs == 0.
+ * tensor_scale: device fp32[1], NVFP4 only. cols % bs == 0. NVFP4_2D outputs are
+ * read as NVFP4 (the layout is the same).
  */
 mxq_status mxq_dequantize(const uint8_t* codes, const uint8_t* scales, mxq_format fmt,
                           int64_t rows, int64_t cols, const float* tensor_scale, void* y,

@@ -44,20 +44,22 @@ mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t col
                           const uint8_t* scales_row, const uint8_t* codes_col,
                           const uint8_t* scales_col, const float* amax) {
   if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;
-  if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4) return MXQ_EINVAL;
+  if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4 && fmt != MXQ_NVFP4_2D) return MXQ_EINVAL;
   if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE && axis != MXQ_BOTH) return MXQ_EINVAL;
   if (rnd != MXQ_RNE && rnd != MXQ_SR) return MXQ_EINVAL;
+  if (fmt == MXQ_NVFP4_2D && rnd == MXQ_SR) return MXQ_EUNSUPPORTED;
   if (rows < 0 || cols < 0) return MXQ_EINVAL;
   if (rows == 0) return MXQ_OK;
   if (!x) return MXQ_EINVAL;
   const bool row = axis & MXQ_ROWWISE, col = axis & MXQ_COLWISE;
   if (row && (!codes_row || !scales_row)) return MXQ_EINVAL;
   if (col && (!codes_col || !scales_col)) return MXQ_EINVAL;
-  if (fmt == MXQ_NVFP4 && !amax) return MXQ_EINVAL;
+  if (fmt != MXQ_MXFP4 && !amax) return MXQ_EINVAL;
   const int64_t bs = fmt == MXQ_MXFP4 ? 32 : 16;
   if (cols == 0 || ldx < cols) return MXQ_ESHAPE;
   if (row && cols % bs) return MXQ_ESHAPE;
   if (col && (rows % bs || cols % 8)) return MXQ_ESHAPE;
+  if (fmt == MXQ_NVFP4_2D && (rows % 16 || cols % 16)) return MXQ_ESHAPE;
   if (too_large(rows, cols)) return MXQ_ESHAPE;
   const int64_t esz = dt == MXQ_BF16 ? 2 : 4;
   if (!aligned(x, 16) || (ldx * esz) % 16) return MXQ_EALIGN;
@@ -76,6 +78,26 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
   if (s != MXQ_OK || rows == 0) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool col = axis & MXQ_COLWISE;
+  if (fmt == MXQ_NVFP4_2D) {
+    TileLaunch a{};
+    a.x = x;
+    a.ldx = ldx;
+    a.rows = rows;
+    a.cols = cols;
+    a.dtype = dt;
+    a.fmt = kNV;
+    a.want_row = axis & MXQ_ROWWISE;
+    a.want_col = col;
+    a.codes_row = codes_row;
+    a.scales_row = scales_row;
+    a.codes_col = codes_col;
+    a.scales_col = scales_col;
+    a.ld_col_codes = rows / 2;
+    a.ld_col_scales = rows / 16;
+    a.amax = amax;
+    a.tensor_scale = tensor_scale;
+    return from_hip(launch_quantize_2d(a, st));
+  }
   if (!col) {
     RowLaunch a{};
     a.x = x;
@@ -142,6 +164,7 @@ mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t c
                             uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
                             uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                             const float* amax, float* tensor_scale, void* stream) {
+  if (fmt == MXQ_NVFP4_2D) return MXQ_EUNSUPPORTED;
   if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4) return MXQ_EINVAL;
   // NVFP4 takes one tensor scale per call, from the amax of the transform along the
   // block axis; the row- and column-wise transforms differ, so one axis per call
@@ -153,6 +176,7 @@ mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t c
 mxq_status mxq_dequantize(const uint8_t* codes, const uint8_t* scales, mxq_format fmt,
                           int64_t rows, int64_t cols, const float* tensor_scale, void* y,
                           mxq_dtype out_dt, void* stream) {
+  if (fmt == MXQ_NVFP4_2D) fmt = MXQ_NVFP4;  // same layout
   if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4) return MXQ_EINVAL;
   if (out_dt != MXQ_BF16 && out_dt != MXQ_F32) return MXQ_EINVAL;
   if (rows < 0 || cols < 0) return MXQ_EINVAL;

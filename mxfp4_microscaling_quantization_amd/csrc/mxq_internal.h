@@ -61,6 +61,9 @@ struct TileLaunch {
 };
 
 hipError_t launch_quantize_tiles(const TileLaunch& a, hipStream_t st);
+// NVFP4 with 16x16 block scales (uses x, ldx, rows, cols, dtype, want_row/col, the
+// outputs, ld_col_*, amax and tensor_scale of the TileLaunch)
+hipError_t launch_quantize_2d(const TileLaunch& a, hipStream_t st);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fmt, int64_t rows,
                              int64_t cols, const float* tensor_scale, void* y, int out_dtype,

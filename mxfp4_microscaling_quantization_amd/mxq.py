@@ -19,11 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
 MXQ_OK, MXQ_EINVAL, MXQ_ESHAPE, MXQ_EALIGN, MXQ_EUNSUPPORTED, MXQ_EHIP = range(6)
 BF16, F32 = 0, 1
-MXFP4, NVFP4 = 0, 1
+MXFP4, NVFP4, NVFP4_2D = 0, 1, 2
 RNE, SR = 0, 1
 ROWWISE, COLWISE, BOTH = 1, 2, 3
 
-_FMT = {"mxfp4": MXFP4, "nvfp4": NVFP4}
+_FMT = {"mxfp4": MXFP4, "nvfp4": NVFP4, "nvfp4_2d": NVFP4_2D}
 _AXIS = {"row": ROWWISE, "col": COLWISE, "both": BOTH}
 _RND = {"rne": RNE, "sr": SR}
 
@@ -120,7 +120,7 @@ def _alloc_outputs(x, rows, cols, fmt, axis):
     if axis & COLWISE:
         cc = torch.empty((cols, rows // 2), dtype=u8, device=dev)
         sc = torch.empty((cols, rows // bs), dtype=u8, device=dev)
-    ts = torch.empty((1,), dtype=torch.float32, device=dev) if fmt == NVFP4 else None
+    ts = torch.empty((1,), dtype=torch.float32, device=dev) if fmt != MXFP4 else None
     return cr, sr, cc, sc, ts
 
 

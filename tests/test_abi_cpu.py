@@ -69,6 +69,12 @@ def q(**kw):
     (dict(ldx=68), mxq.MXQ_EALIGN),              # 136-byte rows
     (dict(cr=FAKE + 4), mxq.MXQ_EALIGN),
     (dict(rows=0, x=None), mxq.MXQ_OK),
+    # NVFP4 with 16x16 block scales: nearest-even only, tensor amax, 16-multiples
+    (dict(fmt=2, rnd=1), mxq.MXQ_EUNSUPPORTED),
+    (dict(fmt=2, amax=None), mxq.MXQ_EINVAL),
+    (dict(fmt=2, rows=40), mxq.MXQ_ESHAPE),
+    (dict(fmt=2, axis=2, cols=72, ldx=72), mxq.MXQ_ESHAPE),
+    (dict(fmt=3), mxq.MXQ_EINVAL),
 ])
 def test_quantize_validation(kw, status):
     assert q(**kw) == status
@@ -87,6 +93,10 @@ def test_other_entry_points_validation():
     # NVFP4 with the transform: one axis per call
     assert L.mxq_rht_quantize(FAKE, 0, 32, 64, 64, 1, 3, 0, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               None) == mxq.MXQ_EUNSUPPORTED
+    assert L.mxq_rht_quantize(FAKE, 0, 32, 64, 64, 2, 1, 0, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              None) == mxq.MXQ_EUNSUPPORTED
+    # 16x16-scaled NVFP4 dequantises as NVFP4 (it needs the tensor scale)
+    assert L.mxq_dequantize(FAKE, FAKE, 2, 4, 64, None, FAKE, 0, None) == mxq.MXQ_EINVAL
     assert L.mxq_rht_amax(FAKE, 0, 32, 64, 64, 3, 0, FAKE, None) == mxq.MXQ_EINVAL
     assert L.mxq_rht_amax(FAKE, 0, 32, 40, 40, 1, 0, FAKE, None) == mxq.MXQ_ESHAPE
     assert L.mxq_rht_amax(FAKE, 0, 24, 64, 64, 2, 0, FAKE, None) == mxq.MXQ_ESHAPE
