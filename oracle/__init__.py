@@ -25,7 +25,9 @@ Readings of points the pages leave open are listed in each function's docstring.
 Parity status per function (what pins it is in tests/test_oracle_*.py):
   formats.*            pinned (brute force, torch casts, closed-form tables)
   mx.*                 pinned (invariants, brute force, hand-worked golden blocks)
-  fp8.*                pinned (torch E4M3 casts, exhaustive code x shift sweep)
+  fp8.*                pinned (torch E4M3 casts, exhaustive code x shift sweep;
+                       the rows-to-columns conversion also by a Fraction brute
+                       force over ragged expert segments)
   rht.*                pinned (scipy Hadamard, orthogonality, inverse, norms)
   nvfp4.*              pinned (Fraction brute force, torch E4M3 cast, invariants)
   philox.philox4x32_10 pinned against rocRAND's independent Philox4x32-10 header
