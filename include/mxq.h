@@ -158,6 +158,36 @@ mxq_status mxq_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* e8m0, int64_t r
                             uint8_t* q8, float* s128, void* stream);
 
 /*
+ * mxq_fp4_row_to_fp8_col - MXFP4 rows -> FP8 columns in one pass (dequantise,
+ * transpose, requantise) for the weight gradient of MoE experts ([HOPPER] section
+ * 2C: fused kernel, ragged per-expert token counts through precomputed offsets, no
+ * padding; Spanish summary, FP4RowToFP8Col).
+ * codes [rows, cols/2] + e8m0 [rows, cols/32]: row-wise MXFP4 of X whose rows are
+ * tokens, expert e owning rows [offsets[e], offsets[e+1]).
+ * q8_col [cols, ld_q8]: E4M3 of X^T; row c holds column c of X at bytes
+ * [0, rows) (the experts' segments side by side); bytes [rows, ld_q8) are not
+ * written.
+ * s_col [cols, ld_s] fp32: per row c, one scale per 128-token group; expert e's
+ * groups start at index sum_{e' < e} ceil(n_e' / 128), the last group of an expert
+ * holds its remaining n_e mod 128 tokens. Entries past the last group are not
+ * written. Scale rule (not fixed by the pages): s = 2^k, k the smallest integer
+ * with max|x| / 2^k <= 448 (k = 0 for an all-zero group); codes are the E4M3
+ * values nearest to x / s (ties to even, subnormals kept, -0 kept). A group that
+ * meets an E8M0 0xFF block gets scale NaN (0x7FC00000) and codes 0x7F.
+ * offsets: device int64 [n_experts + 1], offsets[0] = 0, nondecreasing,
+ * offsets[n_experts] = rows. They are read on the device; values outside [0, rows]
+ * are clamped, so malformed offsets give unspecified output but no access outside
+ * the buffers.
+ * Requirements: cols % 32 == 0, rows < 2^31, 1 <= n_experts <= 4096,
+ * ld_q8 >= rows with ld_q8 % 16 == 0, ld_s >= (rows + 127 * n_experts) / 128
+ * (integer division: enough for any split of the rows). codes and q8_col 16-byte
+ * aligned, s_col 4-byte, offsets 8-byte.
+ */
+mxq_status mxq_fp4_row_to_fp8_col(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t cols,
+                                  const int64_t* offsets, int64_t n_experts, uint8_t* q8_col,
+                                  int64_t ld_q8, float* s_col, int64_t ld_s, void* stream);
+
+/*
  * mxq_rht_quantize - 16-point Hadamard transform fused ahead of quantisation
  * ([MI355X] "Expérience d'investigation": deterministic H16 and random-sign
  * Hadamard; [NVFP4] section 2B: random Hadamard on Wgrad inputs).

@@ -216,6 +216,24 @@ mxq_status mxq_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* e8m0, int64_t r
                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
+mxq_status mxq_fp4_row_to_fp8_col(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t cols,
+                                  const int64_t* offsets, int64_t n_experts, uint8_t* q8_col,
+                                  int64_t ld_q8, float* s_col, int64_t ld_s, void* stream) {
+  if (rows < 0 || cols < 0) return MXQ_EINVAL;
+  if (n_experts < 1 || n_experts > 4096) return MXQ_EINVAL;
+  if (rows == 0) return MXQ_OK;
+  if (!codes || !e8m0 || !offsets || !q8_col || !s_col) return MXQ_EINVAL;
+  if (cols == 0 || cols % 32) return MXQ_ESHAPE;
+  if (rows >= ((int64_t)1 << 31) || too_large(rows, cols)) return MXQ_ESHAPE;
+  if (ld_q8 < rows || ld_s < rc_group_slots(rows, n_experts)) return MXQ_ESHAPE;
+  // the grid enumerates group slots x 256-column tiles
+  if (rc_group_slots(rows, n_experts) * ((cols + 255) / 256) >= ((int64_t)1 << 31)) return MXQ_ESHAPE;
+  if (ld_q8 % 16 || !aligned(codes, 16) || !aligned(q8_col, 16) || !aligned(s_col, 4) || !aligned(offsets, 8))
+    return MXQ_EALIGN;
+  return from_hip(launch_fp4_row_to_fp8_col(codes, e8m0, rows, cols, offsets, (int)n_experts, q8_col, ld_q8,
+                                            s_col, ld_s, reinterpret_cast<hipStream_t>(stream)));
+}
+
 mxq_status mxq_rht_apply(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                          uint32_t sign_mask, float* y, void* stream) {
   if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;

@@ -67,6 +67,7 @@ __device__ __forceinline__ float dppf(float v) {
 // inputs are never passed (NaN blocks are overwritten by the callers).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x2_t __attribute__((ext_vector_type(2)));  // two E4M3 pairs per dword
 
 __device__ __forceinline__ float e8m0_operand(uint32_t byte) { return as_f(byte << 23); }
 

@@ -80,6 +80,13 @@ hipError_t launch_rht_apply(const void* x, int dtype, int64_t rows, int64_t cols
 hipError_t launch_fp8_to_mxfp4(const uint8_t* q8, const float* s128, int64_t rows, int64_t cols,
                                uint8_t* codes, uint8_t* e8m0, hipStream_t st);
 
+// MXFP4 rows -> FP8 columns per 128-token expert group. Group slots of the grid:
+// an upper bound of sum_e ceil(n_e / 128) for any split of the rows into experts.
+inline int64_t rc_group_slots(int64_t rows, int64_t n_experts) { return (rows + 127 * n_experts) / 128; }
+hipError_t launch_fp4_row_to_fp8_col(const uint8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t cols,
+                                     const int64_t* offsets, int n_experts, uint8_t* q8, int64_t ld_q8,
+                                     float* s, int64_t ld_s, hipStream_t st);
+
 hipError_t launch_mxfp4_to_fp8(const uint8_t* codes, const uint8_t* e8m0, int64_t rows,
                                int64_t cols, uint8_t* q8, float* s128, hipStream_t st);
 

@@ -46,6 +46,7 @@ def lib() -> ctypes.CDLL:
     L.mxq_dequantize.argtypes = [vp, vp, i32, i64, i64, vp, vp, i32, vp]
     L.mxq_fp8_to_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.mxq_mxfp4_to_fp8.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    L.mxq_fp4_row_to_fp8_col.argtypes = [vp, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     L.mxq_rht_apply.argtypes = [vp, i32, i64, i64, i64, u32, vp, vp]
     L.mxq_amax.argtypes = [vp, i32, i64, i64, i64, vp, vp]
     L.mxq_rht_amax.argtypes = [vp, i32, i64, i64, i64, i32, u32, vp, vp]
@@ -54,7 +55,7 @@ def lib() -> ctypes.CDLL:
     L.mxq_status_string.argtypes = [i32]
     L.mxq_status_string.restype = ctypes.c_char_p
     for name in ("mxq_quantize", "mxq_rht_quantize", "mxq_dequantize", "mxq_fp8_to_mxfp4",
-                 "mxq_mxfp4_to_fp8", "mxq_rht_apply", "mxq_amax", "mxq_rht_amax"):
+                 "mxq_mxfp4_to_fp8", "mxq_fp4_row_to_fp8_col", "mxq_rht_apply", "mxq_amax", "mxq_rht_amax"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -179,6 +180,28 @@ def mxq_mxfp4_to_fp8(codes: torch.Tensor, e8m0: torch.Tensor, out=None):
                torch.empty((rows, cols // 128), dtype=torch.float32, device=codes.device))
     _check(lib().mxq_mxfp4_to_fp8(_ptr(codes), _ptr(e8m0), rows, cols, _ptr(out[0]), _ptr(out[1]), _stream()))
     return out
+
+
+def fp8_col_scale_slots(rows: int, n_experts: int) -> int:
+    """Scale entries per output row that suffice for any split of `rows` into experts."""
+    return (rows + 127 * n_experts) // 128
+
+
+def mxq_fp4_row_to_fp8_col(codes: torch.Tensor, e8m0: torch.Tensor, offsets: torch.Tensor, out=None):
+    """mxq_fp4_row_to_fp8_col: MXFP4 rows of tokens grouped by expert (device int64
+    offsets [E+1]) -> (E4M3 of X^T [C, R] uint8, fp32 scales [C, S]), one scale per
+    128-token group of an expert; `out` = (q8 [C, ld_q8], scales [C, ld_s])."""
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    n_experts = offsets.numel() - 1
+    if out is None:
+        ld_q8 = (rows + 15) // 16 * 16
+        out = (torch.empty((cols, ld_q8), dtype=torch.uint8, device=codes.device),
+               torch.empty((cols, fp8_col_scale_slots(rows, n_experts)), dtype=torch.float32,
+                           device=codes.device))
+    q8, s = out
+    _check(lib().mxq_fp4_row_to_fp8_col(_ptr(codes), _ptr(e8m0), rows, cols, _ptr(offsets), n_experts,
+                                        _ptr(q8), q8.stride(0), _ptr(s), s.stride(0), _stream()))
+    return q8[:, :rows], s
 
 
 def mxq_rht_apply(x: torch.Tensor, sign_mask: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -63,6 +63,30 @@ def expert_counts(tokens: int, experts: int, seed: int, alpha: float = 0.5) -> n
     return rng.multinomial(tokens, p).astype(np.int64)
 
 
+def mxfp4_codes(rows: int, cols: int, seed: int):
+    """Row-wise MXFP4 data shaped like stored MoE activations, drawn directly (no
+    quantisation happens here): packed codes uint8 [R, C/2] (element 2j in the low
+    nibble) and E8M0 bytes uint8 [R, C/32].
+
+    One random byte per element: its low 4 bits pick the magnitude code 1..7 with
+    weights 1, 2, 2, 3, 3, 3, 2 (roughly the codes of Gaussian blocks scaled to a
+    maximum in [4, 8)), bit 4 the sign, and the element is zero when bits 5-7 are
+    all clear (1/8). A block's byte is 127 plus the rounded log2 of a per-row
+    log-normal(0, 1) magnitude, minus 2, plus a block jitter in {-1, 0, 1}.
+    """
+    rng = np.random.default_rng(seed)
+    lut = np.array([1, 2, 2, 3, 3, 4, 4, 4, 5, 5, 5, 6, 6, 6, 7, 7], dtype=np.uint8)
+    r = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+    nib = lut[r & 15]
+    nib[(r >> 5) == 0] = 0
+    nib |= (r & 16) >> 1
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    row_e = np.round(rng.standard_normal((rows, 1)) / np.log(2.0)).astype(np.int64)
+    jitter = rng.integers(-1, 2, (rows, cols // 32))
+    e8m0 = np.clip(127 - 2 + row_e + jitter, 0, 254).astype(np.uint8)
+    return torch.from_numpy(packed), torch.from_numpy(e8m0)
+
+
 def fp8_from_bf16(x: torch.Tensor):
     """E4M3 codes and per-1x128 power-of-two fp32 scales of a bf16 [R, C] tensor.
 
@@ -94,6 +118,8 @@ class Workload:
     q8: torch.Tensor | None = None         # uint8 E4M3 input (FP8 configs)
     s128: torch.Tensor | None = None       # fp32 [R, C/128] scales
     offsets: np.ndarray | None = None      # expert segment offsets (rows)
+    codes: torch.Tensor | None = None      # packed MXFP4 codes input
+    e8m0: torch.Tensor | None = None       # E8M0 block bytes of `codes`
     rht_seed: int | None = None
     sr_seed: int | None = None
 
@@ -113,6 +139,15 @@ def fp8_moe_experts(rows: int = 65536, cols: int = 7168, experts: int = 256) -> 
     x = moe_activations(rows, cols, 1)
     q8, s = fp8_from_bf16(x)
     return Workload("fp8_mxfp4_65536x7168_256experts", q8=q8, s128=s, offsets=offsets)
+
+
+def fp8_col_experts(rows: int = 65536, cols: int = 7168, experts: int = 256) -> Workload:
+    """MXFP4 token buffer of the MoE layer (the same expert split as fp8_moe_experts)
+    for the rows-to-FP8-columns conversion of the weight gradient."""
+    counts = expert_counts(rows, experts, 1)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    codes, e8m0 = mxfp4_codes(rows, cols, 3)
+    return Workload("fp4_row_to_fp8_col_65536x7168_256experts", codes=codes, e8m0=e8m0, offsets=offsets)
 
 
 def rht_gradients(rows: int = 8192, cols: int = 14336) -> Workload:

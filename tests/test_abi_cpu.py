@@ -20,7 +20,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     L = mxq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -101,6 +101,25 @@ def test_other_entry_points_validation():
     assert L.mxq_rht_amax(FAKE, 0, 32, 40, 40, 1, 0, FAKE, None) == mxq.MXQ_ESHAPE
     assert L.mxq_rht_amax(FAKE, 0, 24, 64, 64, 2, 0, FAKE, None) == mxq.MXQ_ESHAPE
     assert L.mxq_rht_amax(FAKE, 0, 32, 64, 64, 1, 0, None, None) == mxq.MXQ_EINVAL
+    # MXFP4 rows -> FP8 columns: (codes, e8m0, rows, cols, offsets, experts, q8, ld_q8, s, ld_s)
+    rc = L.mxq_fp4_row_to_fp8_col
+    ok = dict(rows=300, cols=64, E=4, ld_q8=304, ld_s=(300 + 127 * 4) // 128)
+    def rcall(**kw):
+        a = dict(ok, codes=FAKE, e8=FAKE, off=FAKE, q8=FAKE, s=FAKE)
+        a.update(kw)
+        return rc(a["codes"], a["e8"], a["rows"], a["cols"], a["off"], a["E"], a["q8"], a["ld_q8"], a["s"],
+                  a["ld_s"], None)
+    assert rcall(rows=0, codes=None) == mxq.MXQ_OK
+    assert rcall(off=None) == mxq.MXQ_EINVAL
+    assert rcall(E=0) == mxq.MXQ_EINVAL
+    assert rcall(E=4097) == mxq.MXQ_EINVAL
+    assert rcall(cols=48) == mxq.MXQ_ESHAPE
+    assert rcall(ld_q8=299) == mxq.MXQ_ESHAPE
+    assert rcall(ld_s=ok["ld_s"] - 1) == mxq.MXQ_ESHAPE
+    assert rcall(rows=2 ** 31, ld_q8=2 ** 31, ld_s=2 ** 24 + 4) == mxq.MXQ_ESHAPE
+    assert rcall(ld_q8=312) == mxq.MXQ_EALIGN
+    assert rcall(off=FAKE + 4) == mxq.MXQ_EALIGN
+    assert rcall(q8=FAKE + 8) == mxq.MXQ_EALIGN
     assert L.mxq_amax(FAKE, 0, 4, 64, 64, None, None) == mxq.MXQ_EINVAL
     assert L.mxq_amax(FAKE, 0, 1, 2 ** 31, 2 ** 31, FAKE, None) == mxq.MXQ_ESHAPE
     assert L.mxq_dequantize(FAKE, FAKE, 0, 1, 2 ** 31, None, FAKE, 0, None) == mxq.MXQ_ESHAPE
