@@ -12,7 +12,11 @@ the 16384 x 7168 bf16 MoE activation tensor (DeepSeek-V3 hidden size, values
   nvfp4_quantize_rne  two-level NVFP4, round to nearest even
   nvfp4_quantize_sr   two-level NVFP4, Philox stochastic rounding
 Throughput counts algorithmic bytes (inputs read + outputs written, as the method
-defines them) over the timed steps. Prints one JSON line.
+defines them) over the timed steps. After the step, the rows beyond it are timed
+at their own shapes (16x16-scaled NVFP4, RHT + NVFP4 column-wise, MXFP4 stochastic
+rounding, MXFP4 rows -> FP8 columns of the 256-expert token buffer) together with
+the fused-vs-unfused ablation of the FP8 <-> MXFP4 conversions. Prints one JSON
+line.
 """
 from __future__ import annotations
 
@@ -252,6 +256,132 @@ def config_report(dev, reps: int = 30) -> list:
     return out
 
 
+def next_rows(dev, x, reps: int = 20) -> tuple[dict, dict]:
+    """The rows beyond the eight-kernel step, each at its own shape with rotating
+    input copies (no input found in a cache): 16x16-scaled NVFP4 of the MoE tensor
+    (both outputs), RHT + NVFP4 column-wise (the weight-gradient recipe), MXFP4 with
+    stochastic rounding, the fused MXFP4-rows -> FP8-columns conversion of the
+    65536 x 7168 token buffer of 256 experts; and the fused-vs-unfused ablation of
+    the two FP8 <-> MXFP4 conversions against op-by-op chains through bf16 (torch
+    casts for the FP8 side), with a bit comparison of the two routes."""
+    import numpy as np
+    import torch
+
+    from mxfp4_microscaling_quantization_amd import mxq, workloads
+
+    E = torch.cuda.Event
+    R, C = x.shape
+    N = R * C
+
+    def timed(fn, n):
+        for k in range(n):
+            fn(k)
+        torch.cuda.synchronize()
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        for k in range(reps):
+            fn(k % n)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    rows = {}
+
+    def row(name, fn, n, nbytes, note):
+        us = timed(fn, n)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows[name] = {"us": round(us, 3), "bytes": nbytes, "GB_s": round(gbs, 1),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "workload": note}
+        print(f"[next] {name:24s} {us:9.2f} us  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}%",
+              file=sys.stderr, flush=True)
+        return us
+
+    n = 3
+    xs = [x.clone() for _ in range(n)]
+    am = [mxq.mxq_amax(v) for v in xs]
+    q2 = [mxq.mxq_quantize(v, "nvfp4_2d", "both", amax=a) for v, a in zip(xs, am)]
+    row("nvfp4_2d_rowcol", lambda k: mxq.mxq_quantize(xs[k], "nvfp4_2d", "both", amax=am[k], out=q2[k]), n,
+        2 * N + 2 * (N // 2 + N // 16) + 4, f"{R}x{C} bf16 MoE tensor, 16x16 block scales, both outputs")
+    del q2
+    mask = mxq.mxq_rht_signs(4)
+    ra = [mxq.mxq_rht_amax(v, mask, "col") for v in xs]
+    rq = [mxq.mxq_rht_quantize(v, mask, "nvfp4", "col", amax=a) for v, a in zip(xs, ra)]
+    row("rht_nvfp4_col", lambda k: mxq.mxq_rht_quantize(xs[k], mask, "nvfp4", "col", amax=ra[k], out=rq[k]), n,
+        2 * N + N // 2 + N // 16 + 4, f"{R}x{C} bf16, H16 along rows, column-wise NVFP4")
+    row("rht_amax_col", lambda k: mxq.mxq_rht_amax(xs[k], mask, "col", out=ra[k]), n, 2 * N + 4,
+        f"{R}x{C} bf16, amax of the column-wise transform")
+    del rq
+    sq = [mxq.mxq_quantize(v, "mxfp4", "row") for v in xs]
+    row("mxfp4_quantize_sr", lambda k: mxq.mxq_quantize(xs[k], "mxfp4", "row", "sr", sr_seed=7, out=sq[k]), n,
+        2 * N + N // 2 + N // 32, f"{R}x{C} bf16, Philox stochastic rounding")
+
+    # ---- fused vs unfused (the pages' kernel-level claim, measured here)
+    abl = {}
+    q8c, s128c = workloads.fp8_from_bf16(x.cpu())
+    q8 = [q8c.to(dev) for _ in range(n)]
+    s128 = [s128c.to(dev) for _ in range(n)]
+    f_out = [mxq.mxq_fp8_to_mxfp4(q8[k], s128[k]) for k in range(n)]
+    yb = [torch.empty((R, C), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+
+    def fp8_unfused(k):
+        v = q8[k].view(torch.float8_e4m3fn).to(torch.bfloat16).view(R, C // 128, 128)
+        torch.mul(v, s128[k].to(torch.bfloat16)[..., None], out=yb[k].view(R, C // 128, 128))
+        return mxq.mxq_quantize(yb[k], "mxfp4", "row", out=sq[k])
+
+    fb = N + 4 * (N // 128) + N // 2 + N // 32
+    t_f = row("fp8_to_mxfp4 (fused)", lambda k: mxq.mxq_fp8_to_mxfp4(q8[k], s128[k], out=f_out[k]), n, fb,
+              f"{R}x{C} E4M3 + 1x128 scales")
+    t_u = row("fp8_to_mxfp4 (unfused)", fp8_unfused, n, fb, "torch E4M3->bf16 cast and scaling, then mxq_quantize")
+    u = fp8_unfused(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(u.codes_row, f_out[0][0]) and torch.equal(u.scales_row, f_out[0][1]))
+    # the bytes an ideal unfused chain must move: FP8 in, bf16 out, bf16 in, MXFP4 out
+    ideal = (N + 4 * (N // 128) + 2 * N + 2 * N + N // 2 + N // 32) / fb
+    abl["fp8_to_mxfp4"] = {"fused_us": round(t_f, 3), "unfused_us": round(t_u, 3),
+                           "speedup": round(t_u / t_f, 3), "same_bits": same,
+                           "unfused_to_fused_bytes": round(ideal, 3)}
+    b_out = [mxq.mxq_mxfp4_to_fp8(*f_out[k]) for k in range(n)]
+    q8o = [torch.empty((R, C), dtype=torch.uint8, device=dev) for _ in range(n)]
+
+    def mx_unfused(k):
+        mxq.mxq_dequantize(f_out[k][0], f_out[k][1], "mxfp4", out=yb[k])
+        smax = f_out[k][1].view(R, C // 128, 4).amax(-1).to(torch.int32)
+        sc = torch.ldexp(torch.ones((), device=dev), (smax - 127).float())
+        q = torch.div(yb[k].view(R, C // 128, 128).float(), sc[..., None]).to(torch.float8_e4m3fn)
+        q8o[k].copy_(q.view(torch.uint8).view(R, C))
+        return q8o[k], sc
+
+    t_f = row("mxfp4_to_fp8 (fused)", lambda k: mxq.mxq_mxfp4_to_fp8(*f_out[k], out=b_out[k]), n, fb,
+              f"{R}x{C} MXFP4 -> E4M3 + 1x128 scales")
+    t_u = row("mxfp4_to_fp8 (unfused)", mx_unfused, n, fb, "mxq_dequantize to bf16, then torch scaling and E4M3 cast")
+    uq, us_ = mx_unfused(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(uq, b_out[0][0]) and torch.equal(us_.float(), b_out[0][1]))
+    abl["mxfp4_to_fp8"] = {"fused_us": round(t_f, 3), "unfused_us": round(t_u, 3),
+                           "speedup": round(t_u / t_f, 3), "same_bits": same,
+                           "unfused_to_fused_bytes": round(ideal, 3)}
+    del xs, am, ra, sq, q8, s128, f_out, yb, b_out, q8o
+    torch.cuda.empty_cache()
+
+    # ---- MXFP4 rows -> FP8 columns on the MoE token buffer
+    w = workloads.fp8_col_experts()
+    Rb, Cb = w.codes.shape[0], w.codes.shape[1] * 2
+    Nb = Rb * Cb
+    n = 2
+    codes = [w.codes.to(dev) for _ in range(n)]
+    e8 = [w.e8m0.to(dev) for _ in range(n)]
+    off = torch.tensor(w.offsets, dtype=torch.int64, device=dev)
+    outs = [mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off) for k in range(n)]
+    outs = [(o[0].as_strided((Cb, Rb), (o[0].stride(0), 1)), o[1]) for o in outs]
+    G = int(np.sum((np.diff(w.offsets) + 127) // 128))
+    row("fp4_row_to_fp8_col", lambda k: mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off, out=outs[k]), n,
+        Nb // 2 + Nb // 32 + Nb + 4 * Cb * G + 8 * len(w.offsets),
+        f"{Rb}x{Cb} MXFP4 tokens of 256 experts (Dirichlet 0.5 split) -> E4M3 of the transpose, {G} groups")
+    del codes, e8, outs
+    torch.cuda.empty_cache()
+    return rows, abl
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +389,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100, help="untimed steps (also bring the clocks up)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="back-to-back launches per kernel for its duration")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the oracle sample (0: skip)")
+    ap.add_argument("--no-next", action="store_true", help="skip the rows beyond the step and the ablation")
     ap.add_argument("--configs", action="store_true",
                     help="also time every configuration at its own shape ([config] lines on stderr)")
     args = ap.parse_args()
@@ -353,6 +484,12 @@ def main() -> int:
                 "frac": d["frac_hbm_peak"], "traffic": traffic, "bytes_per_launch": d["bytes"],
                 "avg_launch_us": d["us"]}
 
+    nxt, abl = (None, None)
+    if not args.no_next:
+        del kernels
+        torch.cuda.empty_cache()
+        nxt, abl = next_rows(dev, x)
+
     cpu = None
     if args.cpu_rows > 0:
         cv, dt = cpu_baseline(x_cpu, q8.cpu(), s128.cpu(), args.cpu_rows)
@@ -382,9 +519,10 @@ def main() -> int:
         "per_kernel": per,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "next_rows": nxt,
+        "ablation_fused_vs_unfused": abl,
     }
     if args.configs:
-        del kernels
         torch.cuda.empty_cache()
         config_report(dev)
     print(json.dumps(line), flush=True)
