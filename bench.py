@@ -388,7 +388,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100, help="untimed steps (also bring the clocks up)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="back-to-back launches per kernel for its duration")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="rows of the oracle sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle sample (0: skip)")
     ap.add_argument("--no-next", action="store_true", help="skip the rows beyond the step and the ablation")
     ap.add_argument("--configs", action="store_true",
                     help="also time every configuration at its own shape ([config] lines on stderr)")
