@@ -125,54 +125,89 @@ __global__ __launch_bounds__(k2dThreads) void quantize_2d_kernel(Params2d p) {
   }
   __syncthreads();
 
-  // ---- phase 3a: row-wise codes (a chunk per task; the scale byte of each
-  // 16-column block on its even chunk)
-  if constexpr (ROW) {
+  // ---- phase 3: one 8x8 block of elements per thread, encoded once. A 16x16 tile
+  // shares one scale, so an element's code is the same in both outputs: the row
+  // codes are stored as they are, and the block's nibbles are transposed in
+  // registers and parked in LDS for the column-wise stores.
+  constexpr int kB8 = k2dTileC / 8;  // 8-column blocks across
+  // column c: rows 8b..8b+7 in dword b; it takes the staged tile's place once every
+  // thread has read its elements
+  uint32_t(*ct)[S::R / 8] = reinterpret_cast<uint32_t(*)[S::R / 8]>(&tile[0][0]);
+  static_assert(k2dTileC * (S::R / 8) * 4 <= sizeof(tile), "the transposed codes fit the tile");
+  {
+    const int rb = (int)t / kB8, cb = (int)t % kB8;
+    const bool valid = rb * 8 < nr && cb * 8 < nc;
+    const uint32_t kb = valid ? kblk[(rb >> 1) * S::BC + (cb >> 1)] : 0u;
+    uint32_t code[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (valid) {
 #pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const uint32_t q = t + j * k2dThreads;
-      const int row = (int)(q / kChunksPerRow), cc = (int)(q % kChunksPerRow);
-      if (row < nr && cc * 8 < nc) {
-        const Raw<T> r = *reinterpret_cast<const Raw<T>*>(&tile[row][swz2<S::G>(row, cc * 8)]);
+      for (int i = 0; i < 8; ++i) {
+        const int row = rb * 8 + i;
+        const Raw<T> r = *reinterpret_cast<const Raw<T>*>(&tile[row][swz2<S::G>(row, cb * 8)]);
         float v[8];
         to_f32(r, v);
-        const uint32_t kb = kblk[(row / 16) * S::BC + cc / 2];
-        const int64_t lr = r0 + row, col = c0 + cc * 8;
-        *reinterpret_cast<uint32_t*>(p.codes_row + (lr * p.cols + col) / 2) = nv2d_codes8(v, kb, nt);
-        if ((cc & 1) == 0) p.scales_row[lr * (p.cols / 16) + col / 16] = (uint8_t)nv2d_byte(kb, nt);
+        code[i] = nv2d_codes8(v, kb, nt);
+      }
+      if constexpr (ROW) {
+        const int64_t col = c0 + cb * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int64_t lr = r0 + rb * 8 + i;
+          *reinterpret_cast<uint32_t*>(p.codes_row + (lr * p.cols + col) / 2) = code[i];
+          if ((cb & 1) == 0) p.scales_row[lr * (p.cols / 16) + col / 16] = (uint8_t)nv2d_byte(kb, nt);
+        }
+      }
+    }
+    if constexpr (COL) {
+      __syncthreads();  // the tile has been read: its space holds the transposed codes
+      if (valid) {
+        // 8x8 nibble transpose: swap 4x4, then 2x2, then 1x1 sub-blocks
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = ((code[i] >> 16) ^ code[i + 4]) & 0x0000FFFFu;
+          code[i] ^= x << 16;
+          code[i + 4] ^= x;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t x = ((code[i + k] >> 8) ^ code[i + k + 2]) & 0x00FF00FFu;
+            code[i + k] ^= x << 8;
+            code[i + k + 2] ^= x;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const uint32_t x = ((code[i] >> 4) ^ code[i + 1]) & 0x0F0F0F0Fu;
+          code[i] ^= x << 4;
+          code[i + 1] ^= x;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ct[cb * 8 + j][rb] = code[j];
       }
     }
   }
 
-  // ---- phase 3b: column-wise codes (one column over 32 rows per task)
+  // ---- phase 4: column-wise stores (one column over 32 rows per task)
   if constexpr (COL) {
+    __syncthreads();
 #pragma unroll 1
     for (int k = t; k < k2dTileC * S::G; k += k2dThreads) {
       const int c = k / S::G, h = k % S::G;
       const int vrows = nr - h * 32;
       if (vrows <= 0 || c >= nc) continue;
-      float v[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int r = h * 32 + i;
-        if constexpr (sizeof(T) == 2) v[i] = as_f((uint32_t)tile[r][swz2<S::G>(r, c)] << 16);
-        else v[i] = tile[r][swz2<S::G>(r, c)];
-      }
       const uint32_t kb0 = kblk[(2 * h) * S::BC + c / 16];
-      const uint32_t kb1 = vrows >= 32 ? kblk[(2 * h + 1) * S::BC + c / 16] : 0u;
-      uint32_t out[4];
-      out[0] = nv2d_codes8(v, kb0, nt);
-      out[1] = nv2d_codes8(v + 8, kb0, nt);
       const int64_t col = c0 + c, grow0 = r0 + h * 32;
       uint8_t* cdst = p.codes_col + col * p.ld_col_codes + grow0 / 2;
       uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
-      *reinterpret_cast<uint2*>(cdst) = make_uint2(out[0], out[1]);
       sdst[grow0 / 16] = (uint8_t)nv2d_byte(kb0, nt);
       if (vrows >= 32) {
-        out[2] = nv2d_codes8(v + 16, kb1, nt);
-        out[3] = nv2d_codes8(v + 24, kb1, nt);
-        *reinterpret_cast<uint2*>(cdst + 8) = make_uint2(out[2], out[3]);
+        const uint32_t kb1 = kblk[(2 * h + 1) * S::BC + c / 16];
+        *reinterpret_cast<uint4*>(cdst) = make_uint4(ct[c][4 * h], ct[c][4 * h + 1], ct[c][4 * h + 2], ct[c][4 * h + 3]);
         sdst[grow0 / 16 + 1] = (uint8_t)nv2d_byte(kb1, nt);
+      } else {
+        *reinterpret_cast<uint2*>(cdst) = make_uint2(ct[c][4 * h], ct[c][4 * h + 1]);
       }
     }
   }
