@@ -262,15 +262,16 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) { return e2m1_r
 // below 2K: there an error of F below K units (y inexact, or the rounding of y + 1)
 // could flip the decision, so the caller keeps the running minimum `low` of those
 // bits and decides the elements exactly when it ends below 2K. Result: the grid
-// value, at most 6.
+// value; 8 stands for 6 (values of [6, 8) that round up), which the callers' scaled
+// E2M1 conversion saturates to 6.
 template <uint32_t K>
 __device__ __forceinline__ float e2m1_sr_carry(float y, uint32_t u, uint32_t& low) {
   const float off = y < 1.0f ? 1.0f : 0.0f;
-  const uint32_t d = ((u >> 10) & 0x3FFFC0u) ^ 0x3FFFC0u;  // 2^22 - 64 - 64 r
-  const uint32_t s = as_u(y + off) + d + (31u + K);
+  // 2^22 - 64 - 64 r + 31 + K, r = u >> 16 (< 2^16: one 24-bit multiply-add)
+  const int d = (int)(u >> 16) * -64 + (int)(0x3FFFC0u + 31u + K);
+  const uint32_t s = as_u(y + off) + (uint32_t)d;
   low = min(low, s & 0x3FFFFFu);
-  const float q = as_f(s & 0xFFC00000u) - off;
-  return as_f(min(as_u(q), 0x40C00000u));
+  return as_f(s & 0xFFC00000u) - off;
 }
 
 // ---------------------------------------------------------------------------
