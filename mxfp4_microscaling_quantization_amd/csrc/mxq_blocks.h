@@ -95,6 +95,18 @@ __device__ __forceinline__ void flip(Raw<float>& r, const SignFlips& f) {
   for (int i = 0; i < 8; ++i) p[i] = as_f(as_u(p[i]) ^ (((f.d[0] >> i) & 1u) << 31));
 }
 
+// Negates all 8 values of a chunk when bit is 1 (a sign shared by the chunk).
+__device__ __forceinline__ void flip_all(Raw<uint16_t>& r, uint32_t bit) {
+  const uint32_t m = bit * 0x80008000u;
+  r.w.x ^= m; r.w.y ^= m; r.w.z ^= m; r.w.w ^= m;
+}
+__device__ __forceinline__ void flip_all(Raw<float>& r, uint32_t bit) {
+  const uint32_t m = bit << 31;
+  float* p = reinterpret_cast<float*>(&r);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = as_f(as_u(p[i]) ^ m);
+}
+
 // z = H16 (s * x) over the 16 elements held by a lane pair (this lane holds
 // positions half*8 .. half*8+7; the signs are already applied). Stages h = 1, 2, 4
 // inside the lane, h = 8 across the pair; fp32. The transform's factor 1/4 is

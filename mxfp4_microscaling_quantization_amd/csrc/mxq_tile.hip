@@ -159,21 +159,45 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   const int64_t r0 = (int64_t)tr * kTileR, c0 = (int64_t)tc * kTileC;
   const int nr = (int)std::min<int64_t>(kTileR, p.rows - r0);
   const int nc = (int)std::min<int64_t>(kTileC, p.cols - c0);
+  // A thread keeps its chunk column cc for every chunk j; its row advances by kRowStep.
+  constexpr int kRowStep = kTileThreads / kChunksPerRow;
+  const int cc = (int)(t % kChunksPerRow), row_t = (int)(t / kChunksPerRow);
+  const bool col_ok = cc * 8 < nc;
+  const T* xt = x + (uint64_t)(r0 + row_t) * (uint64_t)p.ldx + (uint64_t)(c0 + cc * 8);
   Raw<T> cur[kChunks];
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
-    const uint32_t q = t + j * kTileThreads;
-    const int row = (int)(q / kChunksPerRow), cc = (int)(q % kChunksPerRow);
-    if (row < nr && cc * 8 < nc) load_raw(x, (size_t)(r0 + row) * p.ldx + c0 + cc * 8, cur[j]);
+    if (row_t + j * kRowStep < nr && col_ok) load_raw(xt, (uint64_t)(j * kRowStep) * (uint64_t)p.ldx, cur[j]);
     else zero_raw(cur[j]);
   }
 
   // ---- phase 1: row-wise quantise (optional), park raw values in LDS
+  constexpr int bs = FMT == kMX ? 32 : 16;
+  static_assert(kRowStep % 8 == 0, "rows of one thread differ by multiples of 8");
+  const uint32_t csign0 = (p.sign_mask >> (row_t & 15)) & 1u;
+  const uint32_t csign1 = (p.sign_mask >> ((row_t + 8) & 15)) & 1u;
+  const uint64_t col = (uint64_t)(c0 + cc * 8);
+  const uint64_t cols = (uint64_t)p.cols;
+  uint8_t* crow = nullptr;
+  uint8_t* srow = nullptr;
+  if constexpr (ROW) {
+    const uint64_t lr = (uint64_t)(r0 + row_t);  // row within the slab
+    crow = p.codes_row + lr * (cols >> 1) + (col >> 1);
+    srow = p.scales_row + lr * (cols / bs) + col / bs;
+  }
 #pragma unroll
   for (int j = 0; j < kChunks; ++j) {
-    const uint32_t q = t + j * kTileThreads;
-    const int row = (int)(q / kChunksPerRow), cc = (int)(q % kChunksPerRow);
-    *reinterpret_cast<Raw<T>*>(&tile[row][swz<kRowGroups>(row, cc * 8)]) = cur[j];
+    const int row = row_t + j * kRowStep;
+    if constexpr (RHT && COL) {
+      // the column transform's sign of this row (its position mod 16 along the
+      // column) is applied here, once per stored chunk; kRowStep is a multiple of
+      // 8, so a thread's rows take two positions mod 16
+      Raw<T> sr = cur[j];
+      flip_all(sr, ((j * kRowStep) & 8) ? csign1 : csign0);
+      *reinterpret_cast<Raw<T>*>(&tile[row][swz<kRowGroups>(row, cc * 8)]) = sr;
+    } else {
+      *reinterpret_cast<Raw<T>*>(&tile[row][swz<kRowGroups>(row, cc * 8)]) = cur[j];
+    }
     if constexpr (ROW) {
       Raw<T> rr = cur[j];
       if constexpr (RHT) flip(rr, flips);
@@ -181,17 +205,16 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
       to_f32(rr, v);
       if constexpr (RHT) h16_pair(v, t & 1u);
       uint32_t u[8];
-      const int64_t grow = p.row0 + r0 + row;
-      const int64_t col = c0 + cc * 8;
-      if constexpr (SR) sr_words8(p.sr_offset + (uint64_t)(grow * p.cols + col), p.sr_seed, u);
+      if constexpr (SR) {
+        const uint64_t grow = (uint64_t)(p.row0 + r0 + row);
+        sr_words8(p.sr_offset + grow * cols + col, p.sr_seed, u);
+      }
       uint32_t byte, packed;
       if constexpr (FMT == kMX) packed = mx_encode8<SR, RHT ? 2 : 0>(v, u, byte);
       else packed = nv_encode8<SR>(v, u, nt, byte);
-      if (row < nr && cc * 8 < nc) {
-        const int64_t lr = r0 + row;  // row within the slab
-        *reinterpret_cast<uint32_t*>(p.codes_row + (lr * p.cols + col) / 2) = packed;
-        constexpr int bs = FMT == kMX ? 32 : 16;
-        if (col % bs == 0) p.scales_row[lr * (p.cols / bs) + col / bs] = (uint8_t)byte;
+      if (row < nr && col_ok) {
+        *reinterpret_cast<uint32_t*>(crow + (uint64_t)(j * kRowStep) * (cols >> 1)) = packed;
+        if (col % bs == 0) srow[(uint64_t)(j * kRowStep) * (cols / bs)] = (uint8_t)byte;
       }
     }
   }
@@ -208,11 +231,10 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        // the Hadamard sign of row i (position i mod 16 of its chunk) is uniform
-        const uint32_t s = RHT ? ((p.sign_mask >> (i & 15)) & 1u) << 31 : 0u;
+        // the Hadamard signs were applied when the tile was stored
         const int r = h * 32 + i;
-        if constexpr (sizeof(T) == 2) v[i] = as_f(((uint32_t)tile[r][swz<kRowGroups>(r, c)] << 16) ^ s);
-        else v[i] = as_f(as_u(tile[r][swz<kRowGroups>(r, c)]) ^ s);
+        if constexpr (sizeof(T) == 2) v[i] = as_f((uint32_t)tile[r][swz<kRowGroups>(r, c)] << 16);
+        else v[i] = tile[r][swz<kRowGroups>(r, c)];
       }
       if constexpr (RHT) {
         h16_local(v);
