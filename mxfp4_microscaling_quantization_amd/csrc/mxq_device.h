@@ -267,9 +267,15 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) { return e2m1_r
 template <uint32_t K>
 __device__ __forceinline__ float e2m1_sr_carry(float y, uint32_t u, uint32_t& low) {
   const float off = y < 1.0f ? 1.0f : 0.0f;
-  // 2^22 - 64 - 64 r + 31 + K, r = u >> 16 (< 2^16: one 24-bit multiply-add)
-  const int d = (int)(u >> 16) * -64 + (int)(0x3FFFC0u + 31u + K);
-  const uint32_t s = as_u(y + off) + (uint32_t)d;
+  // bits(y + off) - 64 r + 2^22 - 64 + 31 + K, r = u >> 16. The bits of y + off >= 1
+  // exceed 64 r < 2^22, so this is |bits - 64 r| + const: one v_sad_u32 (LLVM has no
+  // builtin for it).
+  // 64 r: the high half of u shifted left by 6, one SDWA shift (written out, as the
+  // compiler would otherwise share a bit-field extract with the exact fallback)
+  uint32_t r64, s;
+  asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+      : "=v"(r64) : "v"(6u), "v"(u));
+  asm("v_sad_u32 %0, %1, %2, %3" : "=v"(s) : "v"(as_u(y + off)), "v"(r64), "v"(0x3FFFC0u + 31u + K));
   low = min(low, s & 0x3FFFFFu);
   return as_f(s & 0xFFC00000u) - off;
 }
