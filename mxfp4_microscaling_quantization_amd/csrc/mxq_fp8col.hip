@@ -230,11 +230,12 @@ __global__ __launch_bounds__(kRcThreads, 3) void fp4_row_to_fp8_col_kernel(RcPar
   const uint32_t colo = 4u * (uint32_t)min(cj, nc / 8 - 1);  // past the tile: repeat its last columns
   const int nbt = nc / 32;                                    // scale blocks in the tile
 
-  // codes of the thread's 16 tokens x 8 columns of group i; rows past the group are
-  // loaded too (they are masked) unless they would pass the tensor's end
+  // codes of the thread's 16 tokens x 8 columns of group i; lanes past the group's
+  // last token read that token again (an L2 hit; their values are masked), so the
+  // next expert's tokens are not fetched for a short group
   auto load_codes = [&](int i, uint32_t* ww) {
     const int64_t g0 = sel_t0[i];
-    const int lim = (int)std::min<int64_t>(kRcGroup, p.rows - g0) - 1;
+    const int lim = sel_n[i] - 1;
     const uint8_t* cb = p.codes + g0 * (int64_t)cstride + c0 / 2 + colo;
 #pragma unroll
     for (int k = 0; k < 16; ++k)
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kRcThreads, 3) void fp4_row_to_fp8_col_kernel(RcPar
   // that each thread then reads its 16 tokens' bytes with one 16-byte LDS read
   auto load_scales = [&](int i, uint32_t* eq) {
     const int64_t g0 = sel_t0[i];
-    const int lim = (int)std::min<int64_t>(kRcGroup, p.rows - g0) - 1;
+    const int lim = sel_n[i] - 1;
     const uint8_t* e8 = p.e8m0 + g0 * (int64_t)estride + c0 / 32 + (uint32_t)min(t >> 1, lim) * estride;
 #pragma unroll
     for (int q = 0; q < 4; ++q) eq[q] = e8[min(4 * (t & 1) + q, nbt - 1)];
