@@ -1,0 +1,90 @@
+"""The boundary's stream contract: every entry point enqueues on the stream it is
+given (torch's current stream in the binding) and keeps no state between calls, so
+results on a side stream, and from two host threads driving two streams at once,
+are bit-identical to the default-stream results."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import require_gpu
+from mxfp4_microscaling_quantization_amd import mxq, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def run_all(x, q8, s128, codes, e8, off, groups, amax):
+    """One call of each entry point; returns every output tensor."""
+    mask = mxq.mxq_rht_signs(4)
+    out = []
+    o = mxq.mxq_quantize(x, "mxfp4", "both")
+    out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col]
+    out.append(mxq.mxq_dequantize(o.codes_row, o.scales_row, "mxfp4", out_dtype=torch.bfloat16))
+    o = mxq.mxq_rht_quantize(x, mask, "mxfp4", "both")
+    out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col]
+    a = mxq.mxq_amax(x)
+    out.append(a)
+    o = mxq.mxq_quantize(x, "nvfp4", "row", "sr", sr_seed=7, sr_offset=3, amax=amax)
+    out += [o.codes_row, o.scales_row, o.tensor_scale]
+    o = mxq.mxq_quantize(x, "nvfp4_2d", "both", amax=amax)
+    out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col]
+    c, e = mxq.mxq_fp8_to_mxfp4(q8, s128)
+    out += [c, e]
+    out += list(mxq.mxq_mxfp4_to_fp8(c, e))
+    q8c, sc = mxq.mxq_fp4_row_to_fp8_col(codes, e8, off)
+    out += [q8c, sc[:, :groups]]  # slots past the last group are not written
+    return out
+
+
+def same(a, b):
+    return all(torch.equal(u.view(torch.uint8), v.view(torch.uint8)) for u, v in zip(a, b))
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    dev = require_gpu()
+    x = workloads.moe_activations(512, 1024, 2).to(dev)
+    q8, s128 = workloads.fp8_from_bf16(x.cpu())
+    w = workloads.fp8_col_experts(rows=1024, cols=512, experts=8)
+    off = torch.tensor(np.asarray(w.offsets, dtype=np.int64), device=dev)
+    groups = int(np.sum((np.diff(np.asarray(w.offsets)) + 127) // 128))
+    return (x, q8.to(dev), s128.to(dev), w.codes.to(dev), w.e8m0.to(dev), off, groups, mxq.mxq_amax(x))
+
+
+def test_side_stream_matches_default_stream(inputs):
+    ref = run_all(*inputs)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        got = run_all(*inputs)
+    st.synchronize()
+    assert same(ref, got)
+
+
+def test_two_host_threads_on_two_streams(inputs):
+    ref = run_all(*inputs)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(k):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                outs = [run_all(*inputs) for _ in range(4)]
+            st.synchronize()
+            results[k] = outs
+        except Exception as exc:  # reported on the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for outs in results.values():
+        for got in outs:
+            assert same(ref, got)
