@@ -186,11 +186,34 @@ def config_report(dev, reps: int = 30) -> list:
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / reps
 
+    def graph_timed(fn, n):
+        # the same launches captured once in a HIP graph: the device time per launch
+        # without the host's per-call launch cost
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(3):
+                fn(k % n)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(reps):
+                fn(k % n)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
     out = []
 
-    def row(cfg, name, fn, n, nbytes, elems):
+    def row(cfg, name, fn, n, nbytes, elems, graph=False):
         warm()
-        us = timed(fn, n)
+        us = graph_timed(fn, n) if graph else timed(fn, n)
         r = {"config": cfg, "kernel": name, "us": round(us, 3), "bytes": nbytes, "GB_s": round(nbytes / us / 1e3, 1),
              "elements_per_s": round(elems / (us * 1e-6), 1), "frac_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
              "buffer_sets": n}
@@ -216,9 +239,13 @@ def config_report(dev, reps: int = 30) -> list:
         qs = [mxq.mxq_quantize(x, "mxfp4", "row") for x in xs]
         ys = [torch.empty_like(x) for x in xs]
         b = 2 * N + N // 2 + N // 32
-        row(cfg, "mxfp4_quantize", lambda k: mxq.mxq_quantize(xs[k], "mxfp4", "row", out=qs[k]), n, b, N)
-        row(cfg, "mxfp4_dequantize",
-            lambda k: mxq.mxq_dequantize(qs[k].codes_row, qs[k].scales_row, "mxfp4", out=ys[k]), n, b, N)
+        qfn = lambda k: mxq.mxq_quantize(xs[k], "mxfp4", "row", out=qs[k])  # noqa: E731
+        dfn = lambda k: mxq.mxq_dequantize(qs[k].codes_row, qs[k].scales_row, "mxfp4", out=ys[k])  # noqa: E731
+        row(cfg, "mxfp4_quantize", qfn, n, b, N)
+        row(cfg, "mxfp4_dequantize", dfn, n, b, N)
+        if cfg == 1:  # a 10.6 MB tensor: the per-call launch cost dominates eager launches
+            row(cfg, "mxfp4_quantize (HIP graph)", qfn, n, b, N, graph=True)
+            row(cfg, "mxfp4_dequantize (HIP graph)", dfn, n, b, N, graph=True)
         del xs, qs, ys
     n = 2
     wl = workloads.fp8_moe_experts()
