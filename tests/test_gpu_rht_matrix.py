@@ -47,3 +47,37 @@ def test_rht_mxfp4_variants_exact_inputs(dt, rnd, axis):
     if axis in ("col", "both"):
         r16t = philox.tensor_r16(C, R, SEED, OFFSET) if sr else None
         check(u8(o.codes_col), u8(o.scales_col), rht.rht_rowwise(x.T.copy(), mask), r16t, what + " col")
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_rht_nvfp4_variants_exact_inputs(dt, rnd, axis):
+    # the tensor scale belongs to the transformed tensor: its amax (exact here) goes
+    # to both sides, and every NVFP4 decision is then taken on exact values
+    dev = require_gpu()
+    rng = np.random.default_rng(19)
+    x = rng.integers(-64, 65, (R, C)) * np.exp2(rng.integers(-3, 4, (R, 1)) - 4.0)
+    xt = torch.from_numpy(x).to(dt)
+    xg = xt.to(dev)
+    mask = rht.sign_mask_from_seed(14)
+    amax = mxq.mxq_rht_amax(xg, mask, axis)
+    a_ref = rht.rht_amax(x, mask, axis)
+    assert float(amax.item()) == a_ref
+    sr = rnd == "sr"
+    o = mxq.mxq_rht_quantize(xg, mask, "nvfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET, amax=amax)
+    if axis == "row":
+        r16 = philox.tensor_r16(R, C, SEED, OFFSET) if sr else None
+        ref_c, ref_s, st = rht.rht_nvfp4_rowwise(x, mask, a_ref, r16)
+        y, codes, scales = rht.rht_rowwise(x, mask), u8(o.codes_row), u8(o.scales_row)
+    else:
+        r16t = philox.tensor_r16(C, R, SEED, OFFSET) if sr else None
+        ref_c, ref_s, st = rht.rht_nvfp4_colwise(x, mask, a_ref, r16t)
+        y, codes, scales = rht.rht_rowwise(x.T.copy(), mask), u8(o.codes_col), u8(o.scales_col)
+    what = f"nvfp4 {dt} {rnd} {axis}"
+    assert float(o.tensor_scale.item()) == float(st), what + " tensor scale"
+    assert np.array_equal(scales, ref_s), what + " scales"
+    g, r = mx.unpack_nibbles(codes), mx.unpack_nibbles(ref_c)
+    assert np.array_equal(g & 7, r & 7), what + " code magnitudes"
+    nz = y != 0
+    assert np.array_equal((g >> 3)[nz], (r >> 3)[nz]), what + " code signs"
