@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t nv2d_byte(uint32_t kb, const NvTensor& t) {
 template <typename T, bool ROW, bool COL>
 __global__ __launch_bounds__(k2dThreads) void quantize_2d_kernel(Params2d p) {
   using S = Shape2d<T>;
-  __shared__ T tile[S::R][k2dTileC];
+  __shared__ T tile[S::R][k2dTileC] __attribute__((aligned(16)));  // read and written as 16-byte chunks
   __shared__ uint32_t part[k2dThreads];  // per-thread partial maxima (|x| bits)
   __shared__ uint32_t kblk[S::B];        // block scale codes (bit 8: NaN block)
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   // LDS tile of raw input values, row-major [128][128], XOR-swizzled columns
   using Shape = TileShape<T, FMT, RHT, ROW>;
   constexpr int kTileR = Shape::R, kTileC = Shape::C, kRowGroups = Shape::G, kVGroup = Shape::V;
-  __shared__ T tile[kTileR][kTileC];
+  __shared__ T tile[kTileR][kTileC] __attribute__((aligned(16)));  // written as 16-byte chunks
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t t = threadIdx.x;
   NvTensor nt;
