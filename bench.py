@@ -415,6 +415,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100, help="untimed steps (also bring the clocks up)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="back-to-back launches per kernel for its duration")
+    ap.add_argument("--single-reps", type=int, default=50,
+                    help="individually timed launches per kernel (median, p10, p90)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle sample (0: skip)")
     ap.add_argument("--no-next", action="store_true", help="skip the rows beyond the step and the ablation")
     ap.add_argument("--configs", action="store_true",
@@ -425,6 +427,7 @@ def main() -> int:
               "build runs on a single GPU; --gpus must be 1", file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
 
     from mxfp4_microscaling_quantization_amd import mxq, workloads
@@ -479,6 +482,18 @@ def main() -> int:
         us = s0.elapsed_time(s1) * 1e3 / args.kernel_reps
         gbs = b / (us * 1e-6) / 1e9
         per[name] = {"us": round(us, 3), "bytes": b, "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        # the distribution of single launches: an event pair around each of
+        # `single_reps` launches (recorded back to back, read after one synchronise)
+        ev = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.single_reps)]
+        for r, (a, z) in enumerate(ev):
+            a.record()
+            fn((r + 1) % sets)
+            z.record()
+        torch.cuda.synchronize()
+        one = np.array([a.elapsed_time(z) * 1e3 for a, z in ev])
+        per[name].update({"us_p10": round(float(np.percentile(one, 10)), 3),
+                          "us_median": round(float(np.median(one)), 3),
+                          "us_p90": round(float(np.percentile(one, 90)), 3), "single_launches": len(one)})
         print(f"[bench] {name:20s} {us:9.2f} us  {gbs:8.1f} GB/s  {100 * gbs / HBM_PEAK_GBS:5.1f}% of 8 TB/s",
               file=sys.stderr, flush=True)
     # reference: a device-to-device copy of 1 GiB (read + write bytes)
