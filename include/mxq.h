@@ -78,8 +78,8 @@ typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
  *   code = sign(x) | E2M1 rounding of |x| / 2^E (nearest, ties to even, saturating
  *   at 6). A block holding NaN or +-Inf gets scale 0xFF and codes 0; an all-zero
  *   block gets scale 0 and sign-only codes.
- * NVFP4 ([NVFP4] section 2A): s_t = RN_fp32(A / 2688) with A = *amax (the tensor's
- *   max |x|, e.g. from mxq_amax); per block of 16 s_b = E4M3 rounding (nearest
+ * NVFP4 ([NVFP4] section 2A): s_t = RN_fp32(A / 2688) with A the tensor's max |x|
+ *   (*amax, or computed first when amax is NULL); per block of 16 s_b = E4M3 rounding (nearest
  *   even, saturating at 448) of the exact quotient max|x_block| / (6 s_t); code =
  *   sign | E2M1 rounding of the exact quotient |x| / (s_b s_t). s_t == 0 gives
  *   scale bytes 0 and sign-only codes, a block with s_b == 0 sign-only codes, a
@@ -103,8 +103,13 @@ typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
  * axis         MXQ_ROWWISE writes codes_row/scales_row, MXQ_COLWISE codes_col/
  *              scales_col, MXQ_BOTH both from a single read of x. Unused output
  *              pointers may be NULL.
- * amax         NVFP4 / NVFP4_2D: device fp32[1] holding the tensor amax (read only).
- * tensor_scale NVFP4 / NVFP4_2D: device fp32[1] receiving s_t (may be NULL).
+ * amax         NVFP4 / NVFP4_2D: device fp32[1] holding the tensor amax (read only), or
+ *              NULL: then the call first computes the amax (as mxq_amax) into the
+ *              tensor_scale slot, turns it into s_t there and quantises from it, all
+ *              on `stream` (no allocation; tensor_scale must then be non-NULL, else
+ *              MXQ_EINVAL). Sharded callers pass the all-reduced amax instead.
+ * tensor_scale NVFP4 / NVFP4_2D: device fp32[1] receiving s_t (may be NULL when amax
+ *              is given). amax and tensor_scale are 4-byte aligned.
  * Shapes: cols % bs == 0 for row-wise; rows % bs == 0 for column-wise outputs.
  */
 mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
@@ -188,45 +193,61 @@ mxq_status mxq_fp4_row_to_fp8_col(const uint8_t* codes, const uint8_t* e8m0, int
                                   int64_t ld_q8, float* s_col, int64_t ld_s, void* stream);
 
 /*
- * mxq_rht_quantize - 16-point Hadamard transform fused ahead of quantisation
- * ([MI355X] "Expérience d'investigation": deterministic H16 and random-sign
- * Hadamard; [NVFP4] section 2B: random Hadamard on Wgrad inputs).
+ * mxq_rht_quantize - 16-point random-sign Hadamard transform fused ahead of
+ * quantisation ([MI355X] "Expérience d'investigation": deterministic H16 and
+ * random-sign Hadamard; [NVFP4] section 2B: random Hadamard on Wgrad inputs).
  * Every aligned 16-element chunk along the block axis (columns for row-wise
  * outputs, rows for column-wise outputs) is replaced by y = (1/4) H16 (s * x),
  * H16 the Sylvester matrix H[i][j] = (-1)^popcount(i & j), s_i = -1 where bit i of
- * sign_mask is set (sign_mask 0 = deterministic H16). y is computed in fp32
- * (butterfly stages 1, 2, 4, 8, then the exact scaling by 1/4) and quantised
- * without an intermediate bf16 rounding. Arguments otherwise as mxq_quantize;
- * rows % 32 (MXFP4) or % 16 (NVFP4) == 0 when a column-wise output is requested.
+ * the sign mask mxq_rht_signs(rht_seed) is set (one sign vector per tensor, drawn
+ * from the seed). y is computed in fp32 (butterfly stages 1, 2, 4, 8, then the
+ * exact scaling by 1/4) and quantised without an intermediate bf16 rounding.
+ * Arguments otherwise as mxq_quantize; rows % 32 (MXFP4) or % 16 (NVFP4) == 0 when
+ * a column-wise output is requested.
  * NVFP4 (the pages' wgrad recipe): the tensor scale belongs to the transformed
- * tensor, so amax must be the amax of y along the requested axis (mxq_rht_amax);
- * the row- and column-wise transforms have different amaxes, so axis must be
+ * tensor, so amax is the amax of y along the requested axis (mxq_rht_amax), or NULL
+ * to have it computed first into the tensor_scale slot (as mxq_quantize does); the
+ * row- and column-wise transforms have different amaxes, so axis must be
  * MXQ_ROWWISE or MXQ_COLWISE (MXQ_BOTH returns MXQ_EUNSUPPORTED). tensor_scale
  * receives s_t of y.
  */
 mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                            mxq_format fmt, mxq_axis axis, uint32_t sign_mask, mxq_round rnd,
+                            mxq_format fmt, mxq_axis axis, uint64_t rht_seed, mxq_round rnd,
                             uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
                             uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                             const float* amax, float* tensor_scale, void* stream);
 
 /*
+ * mxq_rht_quantize_mask - mxq_rht_quantize with the 16-bit sign mask given
+ * directly instead of its seed: sign_mask 0 is the deterministic H16 transform of
+ * [MI355X] "Expérience d'investigation"; mxq_rht_quantize(seed) equals this call
+ * with sign_mask = mxq_rht_signs(seed).
+ */
+mxq_status mxq_rht_quantize_mask(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                                 mxq_format fmt, mxq_axis axis, uint16_t sign_mask, mxq_round rnd,
+                                 uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
+                                 uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                                 const float* amax, float* tensor_scale, void* stream);
+
+/*
  * mxq_rht_apply - the transform alone: y = (1/4) H16 (s * x) on every aligned
- * 16-chunk of each row, written as fp32 [rows, cols] (dense). cols % 16 == 0.
+ * 16-chunk of each row (s from sign_mask, e.g. mxq_rht_signs(rht_seed)), written as
+ * fp32 [rows, cols] (dense). cols % 16 == 0.
  */
 mxq_status mxq_rht_apply(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                         uint32_t sign_mask, float* y, void* stream);
+                         uint16_t sign_mask, float* y, void* stream);
 
 /*
  * mxq_rht_amax - the tensor amax of the transformed tensor, max |y| with
  * y = (1/4) H16 (s * x) taken along the rows (axis MXQ_ROWWISE, cols % 16 == 0) or
  * along the columns (MXQ_COLWISE, rows % 16 == 0, cols % 8 == 0), computed as
- * mxq_rht_quantize computes y (fp32 butterfly). This is the amax NVFP4 with the
- * Hadamard transform takes ([NVFP4] section 2B). Writes fp32 amax_out[0] (device);
- * NaN/Inf propagate as in mxq_amax; rows == 0 writes 0. MXQ_BOTH: MXQ_EINVAL.
+ * mxq_rht_quantize computes y (fp32 butterfly; s from sign_mask, e.g.
+ * mxq_rht_signs(rht_seed)). This is the amax NVFP4 with the Hadamard transform
+ * takes ([NVFP4] section 2B). Writes fp32 amax_out[0] (device); NaN/Inf propagate
+ * as in mxq_amax; rows == 0 writes 0. MXQ_BOTH: MXQ_EINVAL.
  */
 mxq_status mxq_rht_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                        mxq_axis axis, uint32_t sign_mask, float* amax_out, void* stream);
+                        mxq_axis axis, uint16_t sign_mask, float* amax_out, void* stream);
 
 /*
  * mxq_amax - the tensor amax max|x| that NVFP4's tensor scale needs ([NVFP4]
@@ -236,9 +257,11 @@ mxq_status mxq_rht_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
 mxq_status mxq_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                     float* amax_out, void* stream);
 
-/* Host helper: the 16-bit sign mask for a seed, bits 0..15 of word 0 of
- * Philox4x32-10(key = (seed lo, seed hi), counter = 0). */
-uint32_t mxq_rht_signs(uint64_t seed);
+/* Host helper: the Hadamard sign mask of a seed (bit i set: s_i = -1), bits 0..15
+ * of word 0 of Philox4x32-10(key = (seed lo, seed hi), counter = 0). The pages ask
+ * for one random sign vector per tensor but fix no generator; this map is the
+ * library's definition ([MI355X] "Expérience d'investigation"). */
+uint16_t mxq_rht_signs(uint64_t rht_seed);
 
 /* Host helper: a static, human-readable name for a status code. */
 const char* mxq_status_string(mxq_status s);

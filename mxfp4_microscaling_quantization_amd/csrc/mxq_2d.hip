@@ -37,6 +37,7 @@ struct Params2d {
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
   int64_t ld_col_codes, ld_col_scales;
   const float* amax;
+  int st_given;      // *amax holds the tensor scale, not the amax
   float* tensor_scale;
 };
 
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(k2dThreads) void quantize_2d_kernel(Params2d p) {
   __shared__ uint32_t kblk[S::B];        // block scale codes (bit 8: NaN block)
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t t = threadIdx.x;
-  const NvTensor nt = nv_tensor(*p.amax);
+  const NvTensor nt = nv_tensor_load(p.amax, p.st_given);
   if (p.tensor_scale && blockIdx.x == 0 && t == 0) *p.tensor_scale = nt.st;
 
   const uint32_t tr = blockIdx.x / p.tiles_c, tc = blockIdx.x - tr * p.tiles_c;
@@ -235,6 +236,7 @@ hipError_t launch_2d_t(const TileLaunch& a, hipStream_t st) {
     p.ld_col_codes = a.ld_col_codes;
     p.ld_col_scales = a.ld_col_scales;
     p.amax = a.amax;
+    p.st_given = a.st_given ? 1 : 0;
     p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
     const uint32_t grid = (uint32_t)(((nr + S::R - 1) / S::R) * tiles_per_row);
     hipLaunchKernelGGL((quantize_2d_kernel<T, ROW, COL>), dim3(grid), dim3(k2dThreads), 0, st, p);

@@ -42,7 +42,7 @@ uint32_t philox_word0(uint64_t counter, uint64_t seed) {
 mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                           mxq_format fmt, mxq_axis axis, mxq_round rnd, const uint8_t* codes_row,
                           const uint8_t* scales_row, const uint8_t* codes_col,
-                          const uint8_t* scales_col, const float* amax) {
+                          const uint8_t* scales_col, const float* amax, const float* tensor_scale) {
   if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;
   if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4 && fmt != MXQ_NVFP4_2D) return MXQ_EINVAL;
   if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE && axis != MXQ_BOTH) return MXQ_EINVAL;
@@ -54,7 +54,8 @@ mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t col
   const bool row = axis & MXQ_ROWWISE, col = axis & MXQ_COLWISE;
   if (row && (!codes_row || !scales_row)) return MXQ_EINVAL;
   if (col && (!codes_col || !scales_col)) return MXQ_EINVAL;
-  if (fmt != MXQ_MXFP4 && !amax) return MXQ_EINVAL;
+  // NVFP4 without an amax computes it first, in the tensor-scale slot
+  if (fmt != MXQ_MXFP4 && !amax && !tensor_scale) return MXQ_EINVAL;
   const int64_t bs = fmt == MXQ_MXFP4 ? 32 : 16;
   if (cols == 0 || ldx < cols) return MXQ_ESHAPE;
   if (row && cols % bs) return MXQ_ESHAPE;
@@ -65,6 +66,8 @@ mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t col
   if (!aligned(x, 16) || (ldx * esz) % 16) return MXQ_EALIGN;
   if (row && (!aligned(codes_row, 16) || !aligned(scales_row, 4))) return MXQ_EALIGN;
   if (col && (!aligned(codes_col, 16) || !aligned(scales_col, 4))) return MXQ_EALIGN;
+  if (fmt != MXQ_MXFP4 && ((amax && !aligned(amax, 4)) || (tensor_scale && !aligned(tensor_scale, 4))))
+    return MXQ_EALIGN;
   return MXQ_OK;
 }
 
@@ -74,10 +77,24 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
                          uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                          const float* amax, float* tensor_scale, void* stream) {
   mxq_status s = check_quantize(x, dt, rows, cols, ldx, fmt, axis, rnd, codes_row, scales_row,
-                                codes_col, scales_col, amax);
+                                codes_col, scales_col, amax, tensor_scale);
   if (s != MXQ_OK || rows == 0) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool col = axis & MXQ_COLWISE;
+  // NVFP4 with no amax given: the tensor amax (of the transform along the block axis
+  // when the Hadamard transform is fused) is computed into the tensor-scale slot and
+  // turned into s_t there; the quantiser then reads s_t from that slot.
+  bool st_given = false;
+  if (fmt != MXQ_MXFP4 && !amax) {
+    hipError_t e = rht ? launch_rht_amax(x, dt, rows, cols, ldx, axis == MXQ_COLWISE, sign_mask & 0xFFFFu,
+                                         tensor_scale, st)
+                       : launch_amax(x, dt, rows, cols, ldx, tensor_scale, st);
+    if (e == hipSuccess) e = launch_tensor_scale_in_place(tensor_scale, st);
+    if (e != hipSuccess) return MXQ_EHIP;
+    amax = tensor_scale;
+    tensor_scale = nullptr;
+    st_given = true;
+  }
   if (fmt == MXQ_NVFP4_2D) {
     TileLaunch a{};
     a.x = x;
@@ -95,6 +112,7 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
     a.ld_col_codes = rows / 2;
     a.ld_col_scales = rows / 16;
     a.amax = amax;
+    a.st_given = st_given;
     a.tensor_scale = tensor_scale;
     return from_hip(launch_quantize_2d(a, st));
   }
@@ -114,6 +132,7 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
     a.codes = codes_row;
     a.scales = scales_row;
     a.amax = amax;
+    a.st_given = st_given;
     a.tensor_scale = tensor_scale;
     return from_hip(launch_quantize_rows(a, st));
   }
@@ -142,6 +161,7 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
   a.ld_col_codes = rows / 2;
   a.ld_col_scales = rows / bs;
   a.amax = amax;
+  a.st_given = st_given;
   a.tensor_scale = tensor_scale;
   return from_hip(launch_quantize_tiles(a, st));
 }
@@ -159,11 +179,11 @@ mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
                        codes_row, scales_row, codes_col, scales_col, amax, tensor_scale, stream);
 }
 
-mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                            mxq_format fmt, mxq_axis axis, uint32_t sign_mask, mxq_round rnd,
-                            uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
-                            uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
-                            const float* amax, float* tensor_scale, void* stream) {
+mxq_status mxq_rht_quantize_mask(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                                 mxq_format fmt, mxq_axis axis, uint16_t sign_mask, mxq_round rnd,
+                                 uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
+                                 uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                                 const float* amax, float* tensor_scale, void* stream) {
   if (fmt == MXQ_NVFP4_2D) return MXQ_EUNSUPPORTED;
   if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4) return MXQ_EINVAL;
   // NVFP4 takes one tensor scale per call, from the amax of the transform along the
@@ -171,6 +191,16 @@ mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t c
   if (fmt == MXQ_NVFP4 && axis == MXQ_BOTH) return MXQ_EUNSUPPORTED;
   return quantize_impl(x, dt, rows, cols, ldx, fmt, axis, true, sign_mask, rnd, sr_seed, sr_offset,
                        codes_row, scales_row, codes_col, scales_col, amax, tensor_scale, stream);
+}
+
+mxq_status mxq_rht_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                            mxq_format fmt, mxq_axis axis, uint64_t rht_seed, mxq_round rnd,
+                            uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
+                            uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                            const float* amax, float* tensor_scale, void* stream) {
+  return mxq_rht_quantize_mask(x, dt, rows, cols, ldx, fmt, axis, mxq_rht_signs(rht_seed), rnd, sr_seed,
+                               sr_offset, codes_row, scales_row, codes_col, scales_col, amax, tensor_scale,
+                               stream);
 }
 
 mxq_status mxq_dequantize(const uint8_t* codes, const uint8_t* scales, mxq_format fmt,
@@ -235,7 +265,7 @@ mxq_status mxq_fp4_row_to_fp8_col(const uint8_t* codes, const uint8_t* e8m0, int
 }
 
 mxq_status mxq_rht_apply(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                         uint32_t sign_mask, float* y, void* stream) {
+                         uint16_t sign_mask, float* y, void* stream) {
   if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;
   if (rows < 0 || cols < 0) return MXQ_EINVAL;
   if (rows == 0) return MXQ_OK;
@@ -264,7 +294,7 @@ mxq_status mxq_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int
 }
 
 mxq_status mxq_rht_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                        mxq_axis axis, uint32_t sign_mask, float* amax_out, void* stream) {
+                        mxq_axis axis, uint16_t sign_mask, float* amax_out, void* stream) {
   if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;
   if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE) return MXQ_EINVAL;
   if (rows < 0 || cols < 0) return MXQ_EINVAL;
@@ -281,7 +311,7 @@ mxq_status mxq_rht_amax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
   return from_hip(launch_rht_amax(x, dt, rows, cols, ldx, colwise, sign_mask & 0xFFFFu, amax_out, st));
 }
 
-uint32_t mxq_rht_signs(uint64_t seed) { return philox_word0(0, seed) & 0xFFFFu; }
+uint16_t mxq_rht_signs(uint64_t rht_seed) { return (uint16_t)(philox_word0(0, rht_seed) & 0xFFFFu); }
 
 const char* mxq_status_string(mxq_status s) {
   switch (s) {

@@ -344,6 +344,36 @@ __device__ __forceinline__ NvTensor nv_tensor(float amax) {
   return t;
 }
 
+// The same from a tensor scale already computed by nv_tensor (and stored): NaN
+// gives mode 2, zero mode 1, anything else the normalised form.
+__device__ __forceinline__ NvTensor nv_tensor_from_st(float st) {
+  NvTensor t;
+  t.st = st;
+  t.et = 0;
+  t.st_n = 1.0f;
+  if (st != st) {
+    t.mode = 2;
+    t.st = __uint_as_float(0x7FC00000u);
+    return t;
+  }
+  if (st == 0.0f) {
+    t.mode = 1;
+    return t;
+  }
+  t.mode = 0;
+  int e;
+  const float m = frexpf(st, &e);
+  t.st_n = m * 2.0f;
+  t.et = e - 1;
+  return t;
+}
+
+// The tensor scale of a kernel's launch: `src` holds the amax, or (st_given) the
+// tensor scale itself.
+__device__ __forceinline__ NvTensor nv_tensor_load(const float* src, bool st_given) {
+  return st_given ? nv_tensor_from_st(*src) : nv_tensor(*src);
+}
+
 // Exact E4M3 (nearest even, saturating) code of a_n / (6 st_n); a_n >= 0 exact.
 __device__ __forceinline__ uint32_t nv_block_scale(float a_n, float st_n) {
   const float q = a_n * __builtin_amdgcn_rcpf(6.0f * st_n);

@@ -119,7 +119,9 @@ __device__ void find_groups(const RcParams& p, uint32_t gi0, int64_t* sel_t0, in
       const int64_t lo = clamp_token(p.offsets[e], p.rows), hi = clamp_token(p.offsets[e + 1], p.rows);
       const uint32_t cnt = hi > lo ? (uint32_t)((hi - lo + kRcGroup - 1) / kRcGroup) : 0u;
       // the expert's slots g0 .. g0 + cnt - 1 that fall in the workgroup's range
-      const uint32_t s0 = max(g0, gi0), s1 = min(g0 + cnt, gi0 + kRcGroupsPerWG);
+      // (capped at the slot count: with overlapping offsets the experts' groups can
+      // add up to more slots than the scale rows hold)
+      const uint32_t s0 = max(g0, gi0), s1 = min(min(g0 + cnt, gi0 + kRcGroupsPerWG), p.groups);
       for (uint32_t slot = s0; slot < s1; ++slot) {
         const int64_t first = lo + (int64_t)(slot - g0) * kRcGroup;
         sel_t0[slot - gi0] = first;
@@ -239,14 +241,14 @@ __global__ __launch_bounds__(kRcThreads, 3) void fp4_row_to_fp8_col_kernel(RcPar
     const uint8_t* cb = p.codes + g0 * (int64_t)cstride + c0 / 2 + colo;
 #pragma unroll
     for (int k = 0; k < 16; ++k)
-      ww[k] = *reinterpret_cast<const uint32_t*>(cb + (uint32_t)min(16 * ig + k, lim) * cstride);
+      ww[k] = *reinterpret_cast<const uint32_t*>(cb + (uint64_t)min(16 * ig + k, lim) * cstride);
   };
   // scale bytes travel through LDS (thread t stages four blocks of token t / 2), so
   // that each thread then reads its 16 tokens' bytes with one 16-byte LDS read
   auto load_scales = [&](int i, uint32_t* eq) {
     const int64_t g0 = sel_t0[i];
     const int lim = sel_n[i] - 1;
-    const uint8_t* e8 = p.e8m0 + g0 * (int64_t)estride + c0 / 32 + (uint32_t)min(t >> 1, lim) * estride;
+    const uint8_t* e8 = p.e8m0 + g0 * (int64_t)estride + c0 / 32 + (uint64_t)min(t >> 1, lim) * estride;
 #pragma unroll
     for (int q = 0; q < 4; ++q) eq[q] = e8[min(4 * (t & 1) + q, nbt - 1)];
   };

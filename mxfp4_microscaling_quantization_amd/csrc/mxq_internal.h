@@ -35,7 +35,8 @@ struct RowLaunch {
   uint64_t sr_seed, sr_base;
   uint8_t* codes;
   uint8_t* scales;
-  const float* amax;
+  const float* amax;   // NVFP4: the tensor amax, or the tensor scale when st_given
+  bool st_given;
   float* tensor_scale;
 };
 
@@ -56,7 +57,8 @@ struct TileLaunch {
   int64_t row0;                    // first row of this slab in the whole tensor
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
   int64_t ld_col_codes, ld_col_scales;  // row strides of the column-wise outputs
-  const float* amax;
+  const float* amax;   // NVFP4: the tensor amax, or the tensor scale when st_given
+  bool st_given;
   float* tensor_scale;
 };
 
@@ -71,6 +73,9 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fm
 
 hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                        float* amax_out, hipStream_t st);
+// Replaces the amax held in *slot by the NVFP4 tensor scale RN_fp32(amax / 2688)
+// (NaN for a non-finite amax), in place: one thread.
+hipError_t launch_tensor_scale_in_place(float* slot, hipStream_t st);
 
 hipError_t launch_rht_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, bool colwise,
                            uint32_t sign_mask, float* amax_out, hipStream_t st);

@@ -31,6 +31,7 @@ struct RowParams {
   uint64_t sr_seed, sr_base;
   uint32_t sign_mask;
   const float* amax;
+  int st_given;      // *amax holds the tensor scale, not the amax
   float* tensor_scale;
 };
 
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
   const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
   NvTensor nt;
   if constexpr (FMT == kNV) {
-    nt = nv_tensor(*p.amax);
+    nt = nv_tensor_load(p.amax, p.st_given);
     if (p.tensor_scale && blockIdx.x == 0 && threadIdx.x == 0) *p.tensor_scale = nt.st;
     if constexpr (RHT) nv_tensor_times4(nt);
   }
@@ -110,6 +111,7 @@ static hipError_t launch_rows_t(const RowLaunch& a, hipStream_t st) {
     p.sr_base = a.sr_base + (uint64_t)(r0 * a.cols);
     p.sign_mask = a.sign_mask;
     p.amax = a.amax;
+    p.st_given = a.st_given ? 1 : 0;
     p.tensor_scale = r0 == 0 ? a.tensor_scale : nullptr;
     const uint32_t grid = (p.chunks + kChunksPerWG - 1) / kChunksPerWG;
     const bool contig = a.ldx == a.cols;
@@ -346,6 +348,13 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fm
 // per workgroup on a slot the preceding one-thread kernel zeroed.
 
 __global__ void amax_init_kernel(float* out) { *reinterpret_cast<uint32_t*>(out) = 0u; }
+
+__global__ void tensor_scale_in_place_kernel(float* slot) { *slot = nv_tensor(*slot).st; }
+
+hipError_t launch_tensor_scale_in_place(float* slot, hipStream_t st) {
+  hipLaunchKernelGGL(tensor_scale_in_place_kernel, dim3(1), dim3(1), 0, st, slot);
+  return hipGetLastError();
+}
 
 template <typename T, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void amax_kernel(RowParams p, uint32_t* out) {

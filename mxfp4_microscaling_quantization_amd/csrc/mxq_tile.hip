@@ -50,6 +50,7 @@ struct TileParams {
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
   int64_t ld_col_codes, ld_col_scales;
   const float* amax;
+  int st_given;      // *amax holds the tensor scale, not the amax
   float* tensor_scale;
 };
 
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   const uint32_t t = threadIdx.x;
   NvTensor nt;
   if constexpr (FMT == kNV) {
-    nt = nv_tensor(*p.amax);
+    nt = nv_tensor_load(p.amax, p.st_given);
     if (p.tensor_scale && blockIdx.x == 0 && t == 0) *p.tensor_scale = nt.st;
     if constexpr (RHT) nv_tensor_times4(nt);
   }
@@ -303,6 +304,7 @@ static hipError_t launch_tiles_shape(const TileLaunch& a, hipStream_t st) {
     p.ld_col_codes = a.ld_col_codes;
     p.ld_col_scales = a.ld_col_scales;
     p.amax = a.amax;
+    p.st_given = a.st_given ? 1 : 0;
     p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
     const uint32_t grid = 8u * kVGroup * ((p.groups + 7u) / 8u);
     hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, ROW, true>), dim3(grid), dim3(kTileThreads), 0, st, p);

@@ -39,22 +39,24 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m mxfp4_microscaling_quantization_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64, u32, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
+    vp, i32, i64, u16, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint16, ctypes.c_uint64
     L.mxq_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, i32, u64, u64, vp, vp, vp, vp, vp, vp, vp]
-    L.mxq_rht_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, u32, i32, u64, u64, vp, vp, vp, vp,
+    L.mxq_rht_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, u64, i32, u64, u64, vp, vp, vp, vp,
                                    vp, vp, vp]
+    L.mxq_rht_quantize_mask.argtypes = [vp, i32, i64, i64, i64, i32, i32, u16, i32, u64, u64, vp, vp, vp,
+                                        vp, vp, vp, vp]
     L.mxq_dequantize.argtypes = [vp, vp, i32, i64, i64, vp, vp, i32, vp]
     L.mxq_fp8_to_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.mxq_mxfp4_to_fp8.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.mxq_fp4_row_to_fp8_col.argtypes = [vp, vp, i64, i64, vp, i64, vp, i64, vp, i64, vp]
-    L.mxq_rht_apply.argtypes = [vp, i32, i64, i64, i64, u32, vp, vp]
+    L.mxq_rht_apply.argtypes = [vp, i32, i64, i64, i64, u16, vp, vp]
     L.mxq_amax.argtypes = [vp, i32, i64, i64, i64, vp, vp]
-    L.mxq_rht_amax.argtypes = [vp, i32, i64, i64, i64, i32, u32, vp, vp]
+    L.mxq_rht_amax.argtypes = [vp, i32, i64, i64, i64, i32, u16, vp, vp]
     L.mxq_rht_signs.argtypes = [u64]
-    L.mxq_rht_signs.restype = u32
+    L.mxq_rht_signs.restype = u16
     L.mxq_status_string.argtypes = [i32]
     L.mxq_status_string.restype = ctypes.c_char_p
-    for name in ("mxq_quantize", "mxq_rht_quantize", "mxq_dequantize", "mxq_fp8_to_mxfp4",
+    for name in ("mxq_quantize", "mxq_rht_quantize", "mxq_rht_quantize_mask", "mxq_dequantize", "mxq_fp8_to_mxfp4",
                  "mxq_mxfp4_to_fp8", "mxq_fp4_row_to_fp8_col", "mxq_rht_apply", "mxq_amax", "mxq_rht_amax"):
         getattr(L, name).restype = i32
     _lib = L
@@ -128,7 +130,8 @@ def _alloc_outputs(x, rows, cols, fmt, axis):
 def mxq_quantize(x: torch.Tensor, fmt: str = "mxfp4", axis: str = "row", rnd: str = "rne",
                  sr_seed: int = 0, sr_offset: int = 0, amax: Optional[torch.Tensor] = None,
                  out: Optional[Quantized] = None) -> Quantized:
-    """mxq_quantize: MXFP4/NVFP4 quantisation (NVFP4 takes the tensor amax, e.g. from mxq_amax)."""
+    """mxq_quantize: MXFP4/NVFP4 quantisation. NVFP4 takes the tensor amax (e.g. from
+    mxq_amax), or computes it first when `amax` is None."""
     rows, cols, ldx = _rows_view(x)
     f, a, r = _FMT[fmt], _AXIS[axis], _RND[rnd]
     o = out if out is not None else Quantized(*_alloc_outputs(x, rows, cols, f, a))
@@ -138,16 +141,31 @@ def mxq_quantize(x: torch.Tensor, fmt: str = "mxfp4", axis: str = "row", rnd: st
     return o
 
 
-def mxq_rht_quantize(x: torch.Tensor, sign_mask: int, fmt: str = "mxfp4", axis: str = "row",
+def mxq_rht_quantize(x: torch.Tensor, rht_seed: int, fmt: str = "mxfp4", axis: str = "row",
                      rnd: str = "rne", sr_seed: int = 0, sr_offset: int = 0,
                      amax: Optional[torch.Tensor] = None, out: Optional[Quantized] = None) -> Quantized:
-    """mxq_rht_quantize: 16-point Hadamard (sign mask bit i -> s_i = -1) fused ahead of quantisation."""
+    """mxq_rht_quantize: random-sign 16-point Hadamard (signs drawn from `rht_seed`,
+    mxq_rht_signs) fused ahead of quantisation."""
     rows, cols, ldx = _rows_view(x)
     f, a, r = _FMT[fmt], _AXIS[axis], _RND[rnd]
     o = out if out is not None else Quantized(*_alloc_outputs(x, rows, cols, f, a))
-    _check(lib().mxq_rht_quantize(_ptr(x), _dtype_code(x), rows, cols, ldx, f, a, sign_mask, r, sr_seed,
+    _check(lib().mxq_rht_quantize(_ptr(x), _dtype_code(x), rows, cols, ldx, f, a, rht_seed, r, sr_seed,
                                   sr_offset, _ptr(o.codes_row), _ptr(o.scales_row), _ptr(o.codes_col),
                                   _ptr(o.scales_col), _ptr(amax), _ptr(o.tensor_scale), _stream()))
+    return o
+
+
+def mxq_rht_quantize_mask(x: torch.Tensor, sign_mask: int, fmt: str = "mxfp4", axis: str = "row",
+                          rnd: str = "rne", sr_seed: int = 0, sr_offset: int = 0,
+                          amax: Optional[torch.Tensor] = None, out: Optional[Quantized] = None) -> Quantized:
+    """mxq_rht_quantize_mask: as mxq_rht_quantize with the sign mask given directly
+    (bit i -> s_i = -1; 0 = the deterministic H16)."""
+    rows, cols, ldx = _rows_view(x)
+    f, a, r = _FMT[fmt], _AXIS[axis], _RND[rnd]
+    o = out if out is not None else Quantized(*_alloc_outputs(x, rows, cols, f, a))
+    _check(lib().mxq_rht_quantize_mask(_ptr(x), _dtype_code(x), rows, cols, ldx, f, a, sign_mask, r, sr_seed,
+                                       sr_offset, _ptr(o.codes_row), _ptr(o.scales_row), _ptr(o.codes_col),
+                                       _ptr(o.scales_col), _ptr(amax), _ptr(o.tensor_scale), _stream()))
     return o
 
 

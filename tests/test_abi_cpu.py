@@ -15,12 +15,12 @@ HEADER = os.path.join(ROOT, "include", "mxq.h")
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:mxq_status|uint32_t|const char\*)\s+(mxq_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:mxq_status|uint16_t|const char\*)\s+(mxq_\w+)\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     L = mxq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -35,7 +35,9 @@ def test_status_strings():
 def test_rht_signs_match_oracle():
     from oracle import rht
     for seed in (0, 1, 4, 7, 2 ** 40 + 3, 2 ** 64 - 1):
-        assert mxq.mxq_rht_signs(seed) == rht.sign_mask_from_seed(seed)
+        m = mxq.mxq_rht_signs(seed)
+        assert 0 <= m < 2 ** 16
+        assert m == rht.sign_mask_from_seed(seed)
 
 
 FAKE = 0x10000  # a 16-byte aligned, never dereferenced address
@@ -59,7 +61,9 @@ def q(**kw):
     (dict(rows=-1), mxq.MXQ_EINVAL),
     (dict(cr=None), mxq.MXQ_EINVAL),
     (dict(axis=2, sc=None), mxq.MXQ_EINVAL),
-    (dict(fmt=1, amax=None), mxq.MXQ_EINVAL),
+    (dict(fmt=1, amax=None), mxq.MXQ_EINVAL),     # no amax and no slot to compute it in
+    (dict(fmt=1, amax=None, ts=FAKE + 2), mxq.MXQ_EALIGN),
+    (dict(fmt=1, amax=FAKE + 1, ts=FAKE), mxq.MXQ_EALIGN),
     (dict(cols=48), mxq.MXQ_ESHAPE),             # not a multiple of 32
     (dict(ldx=32), mxq.MXQ_ESHAPE),
     (dict(axis=2, rows=48), mxq.MXQ_ESHAPE),
@@ -72,6 +76,7 @@ def q(**kw):
     # NVFP4 with 16x16 block scales: nearest-even only, tensor amax, 16-multiples
     (dict(fmt=2, rnd=1), mxq.MXQ_EUNSUPPORTED),
     (dict(fmt=2, amax=None), mxq.MXQ_EINVAL),
+    (dict(fmt=2, amax=None, ts=FAKE + 1), mxq.MXQ_EALIGN),
     (dict(fmt=2, rows=40), mxq.MXQ_ESHAPE),
     (dict(fmt=2, axis=2, cols=72, ldx=72), mxq.MXQ_ESHAPE),
     (dict(fmt=3), mxq.MXQ_EINVAL),
@@ -95,6 +100,15 @@ def test_other_entry_points_validation():
                               None) == mxq.MXQ_EUNSUPPORTED
     assert L.mxq_rht_quantize(FAKE, 0, 32, 64, 64, 2, 1, 0, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               None) == mxq.MXQ_EUNSUPPORTED
+    # the seed is a full 64-bit value; the mask form takes the 16-bit mask
+    assert L.mxq_rht_quantize(FAKE, 0, 32, 64, 64, 1, 3, 2 ** 64 - 1, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, None) == mxq.MXQ_EUNSUPPORTED
+    assert L.mxq_rht_quantize_mask(FAKE, 0, 32, 64, 64, 1, 3, 0xFFFF, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, None) == mxq.MXQ_EUNSUPPORTED
+    assert L.mxq_rht_quantize_mask(FAKE, 0, 32, 48, 48, 0, 1, 0, 0, 0, 0, FAKE, FAKE, None, None, None,
+                                   None, None) == mxq.MXQ_ESHAPE
+    assert L.mxq_rht_quantize(FAKE, 0, 32, 64, 64, 1, 2, 5, 0, 0, 0, None, None, FAKE, FAKE, None,
+                              None, None) == mxq.MXQ_EINVAL  # NVFP4: no amax and no tensor-scale slot
     # 16x16-scaled NVFP4 dequantises as NVFP4 (it needs the tensor scale)
     assert L.mxq_dequantize(FAKE, FAKE, 2, 4, 64, None, FAKE, 0, None) == mxq.MXQ_EINVAL
     assert L.mxq_rht_amax(FAKE, 0, 32, 64, 64, 3, 0, FAKE, None) == mxq.MXQ_EINVAL

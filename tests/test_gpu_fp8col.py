@@ -137,3 +137,52 @@ def test_full_65536x7168_256_experts_sampled():
         assert_equal_bits(u8(q8[32 * b:32 * b + 32]), rq, f"block {b} E4M3")
         assert_equal_bits(s[32 * b:32 * b + 32, :G].cpu().view(torch.int32).numpy().view(np.uint32), rs,
                           f"block {b} scales")
+
+
+def test_overlapping_offsets_stay_inside_the_buffers():
+    # malformed offsets (experts that overlap) give unspecified values but must not
+    # write outside the outputs: here the experts' groups add up to more than the
+    # scale slots the call sizes for, and every slot past them, and every byte past
+    # the last token, must keep its sentinel
+    dev = require_gpu()
+    rng = np.random.default_rng(17)
+    R, C = 300, 64
+    codes, e8m0 = random_codes(rng, R, C)
+    for offs in ([0, R, 0, R, 0, R], [0, R, 0, R], [0, 290, 10, R]):
+        E = len(offs) - 1
+        S = mxq.fp8_col_scale_slots(R, E)
+        ld = (R + 15) // 16 * 16
+        q8 = torch.full((C, ld + 16), SENTINEL, dtype=torch.uint8, device=dev)
+        s_big = torch.zeros((C, S + 8), dtype=torch.float32, device=dev)
+        s_big.view(torch.int32).fill_(0x5A5A5A5A)
+        off = torch.tensor(np.asarray(offs, dtype=np.int64), device=dev)
+        mxq.mxq_fp4_row_to_fp8_col(torch.as_tensor(codes).to(dev), torch.as_tensor(e8m0).to(dev), off,
+                                   out=(q8[:, :ld], s_big[:, :S]))
+        torch.cuda.synchronize()
+        assert (u8(q8)[:, R:] == SENTINEL).all(), offs
+        assert (s_big.cpu().view(torch.int32).numpy().view(np.uint32)[:, S:] == 0x5A5A5A5A).all(), offs
+
+
+def test_wide_rows_address_tokens_in_64_bits():
+    # 128 tokens of 3 * 2^25 columns: the codes of token 86 and later lie more than
+    # 2^32 bytes past the group's first token, so token offsets must be formed in 64
+    # bits; sampled column tiles at both ends and in the middle against the oracle
+    dev = require_gpu()
+    R, C = 128, 3 * 2 ** 25
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    codes = torch.randint(0, 256, (R, C // 2), dtype=torch.uint8, device=dev, generator=g)
+    e8m0 = torch.randint(115, 135, (R, C // 32), dtype=torch.uint8, device=dev, generator=g)
+    off = torch.tensor([0, 40, R], dtype=torch.int64, device=dev)
+    q8, s = mxq.mxq_fp4_row_to_fp8_col(codes, e8m0, off)
+    torch.cuda.synchronize()
+    for c0 in (0, C // 2 + 256 * 7, C - 256):
+        sl = slice(c0, c0 + 256)
+        pc = u8(codes[:, c0 // 2:(c0 + 256) // 2])
+        pe = u8(e8m0[:, c0 // 32:(c0 + 256) // 32])
+        rq, rs = fp8.mxfp4_rows_to_fp8_cols(pc, pe, np.array([0, 40, R], dtype=np.int64))
+        assert_equal_bits(u8(q8[sl]), rq, f"wide rows E4M3, columns {c0}..")
+        assert_equal_bits(s[sl, :rs.shape[1]].cpu().view(torch.int32).numpy().view(np.uint32), rs,
+                          f"wide rows scales, columns {c0}..")
+    del codes, e8m0, q8, s
+    torch.cuda.empty_cache()

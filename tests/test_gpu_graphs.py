@@ -16,15 +16,18 @@ R, C = 512, 1024
 
 
 def calls(x, q8, s128):
-    mask = mxq.mxq_rht_signs(9)
     out = []
     o = mxq.mxq_quantize(x, "mxfp4", "row")
     out += [o.codes_row, o.scales_row]
     out.append(mxq.mxq_dequantize(o.codes_row, o.scales_row, "mxfp4", out_dtype=torch.float32))
-    o = mxq.mxq_rht_quantize(x, mask, "mxfp4", "both")
+    o = mxq.mxq_rht_quantize(x, 9, "mxfp4", "both")
     out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col]
     a = mxq.mxq_amax(x)
-    out.append(a)
+    out.append(a)  # output 7
+    o = mxq.mxq_rht_quantize(x, 9, "nvfp4", "row")  # amax of the transform computed first
+    out += [o.codes_row, o.scales_row, o.tensor_scale]
+    o = mxq.mxq_quantize(x, "nvfp4", "both", "sr", sr_seed=5)  # tensor amax computed first
+    out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col, o.tensor_scale]
     for rnd in ("rne", "sr"):
         o = mxq.mxq_quantize(x, "nvfp4", "col", rnd, sr_seed=11, sr_offset=0, amax=a)
         out += [o.codes_col, o.scales_col, o.tensor_scale]

@@ -85,7 +85,7 @@ def test_rht_quantize_small(axis):
     dev = require_gpu()
     w = workloads.heavy_tailed_gradients(512, 1024, 4)
     mask = rht.sign_mask_from_seed(4)
-    o = mxq.mxq_rht_quantize(w.to(dev), mask, "mxfp4", axis)
+    o = mxq.mxq_rht_quantize_mask(w.to(dev), mask, "mxfp4", axis)
     x64 = f64(w)
     if axis in ("row", "both"):
         compare(u8(o.codes_row), u8(o.scales_row), rht.rht_rowwise(x64, mask), x64, f"rht {axis} row")
@@ -101,7 +101,7 @@ def test_deterministic_h16_equals_mask_zero_and_bitexact_on_exact_inputs():
     rng = np.random.default_rng(5)
     x = rng.integers(-64, 65, (64, 256)) * 2.0 ** -4
     xt = torch.from_numpy(x).to(torch.bfloat16)
-    o = mxq.mxq_rht_quantize(xt.to(dev), 0, "mxfp4", "both")
+    o = mxq.mxq_rht_quantize_mask(xt.to(dev), 0, "mxfp4", "both")
     rc, rs = rht.rht_mxfp4_rowwise(x, 0)
     cc, cs = rht.rht_mxfp4_colwise(x, 0)
     # exact transform: the only permitted difference is the sign of an exact zero
@@ -120,7 +120,7 @@ def test_rht_gradients_8192x14336_sampled():
     w = workloads.rht_gradients()
     mask = rht.sign_mask_from_seed(w.rht_seed)
     xg = w.x.to(dev)
-    o = mxq.mxq_rht_quantize(xg, mask, "mxfp4", "both")
+    o = mxq.mxq_rht_quantize_mask(xg, mask, "mxfp4", "both")
     rows = sample_rows(8192, 24)
     x64 = f64(w.x[rows])
     compare(u8(o.codes_row[rows]), u8(o.scales_row[rows]), rht.rht_rowwise(x64, mask), x64,

@@ -39,7 +39,7 @@ def test_rht_mxfp4_variants_exact_inputs(dt, rnd, axis):
     assert np.array_equal(f64(xt), x)  # exact in both input types
     mask = rht.sign_mask_from_seed(13)
     sr = rnd == "sr"
-    o = mxq.mxq_rht_quantize(xt.to(dev), mask, "mxfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET)
+    o = mxq.mxq_rht_quantize_mask(xt.to(dev), mask, "mxfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET)
     what = f"{dt} {rnd} {axis}"
     if axis in ("row", "both"):
         r16 = philox.tensor_r16(R, C, SEED, OFFSET) if sr else None
@@ -65,7 +65,7 @@ def test_rht_nvfp4_variants_exact_inputs(dt, rnd, axis):
     a_ref = rht.rht_amax(x, mask, axis)
     assert float(amax.item()) == a_ref
     sr = rnd == "sr"
-    o = mxq.mxq_rht_quantize(xg, mask, "nvfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET, amax=amax)
+    o = mxq.mxq_rht_quantize_mask(xg, mask, "nvfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET, amax=amax)
     if axis == "row":
         r16 = philox.tensor_r16(R, C, SEED, OFFSET) if sr else None
         ref_c, ref_s, st = rht.rht_nvfp4_rowwise(x, mask, a_ref, r16)

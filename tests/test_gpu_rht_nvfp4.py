@@ -86,7 +86,7 @@ def test_rht_nvfp4_random(axis):
     mask = rht.sign_mask_from_seed(4)
     xg = w.to(dev)
     amax = mxq.mxq_rht_amax(xg, mask, axis)
-    o = mxq.mxq_rht_quantize(xg, mask, "nvfp4", axis, amax=amax)
+    o = mxq.mxq_rht_quantize_mask(xg, mask, "nvfp4", axis, amax=amax)
     a = float(amax.item())
     x64 = f64(w)
     if axis == "row":
@@ -109,7 +109,7 @@ def test_rht_nvfp4_bitexact_on_exact_inputs(rnd):
         amax = mxq.mxq_rht_amax(xt.to(dev), mask, axis)
         a = float(amax.item())
         assert a == rht.rht_amax(x, mask, axis)
-        o = mxq.mxq_rht_quantize(xt.to(dev), mask, "nvfp4", axis, rnd, sr_seed=21, sr_offset=3, amax=amax)
+        o = mxq.mxq_rht_quantize_mask(xt.to(dev), mask, "nvfp4", axis, rnd, sr_seed=21, sr_offset=3, amax=amax)
         if axis == "row":
             r16 = philox.tensor_r16(64, 256, seed=21, offset=3) if rnd == "sr" else None
             rc, rs, _ = rht.rht_nvfp4_rowwise(x, mask, amax=a, r16=r16)
@@ -136,7 +136,7 @@ def test_rht_nvfp4_gradients_8192x14336_colwise_sampled():
     mask = rht.sign_mask_from_seed(w.rht_seed)
     xg = w.x.to(dev)
     amax = mxq.mxq_rht_amax(xg, mask, "col")
-    o = mxq.mxq_rht_quantize(xg, mask, "nvfp4", "col", amax=amax)
+    o = mxq.mxq_rht_quantize_mask(xg, mask, "nvfp4", "col", amax=amax)
     cols = sample_rows(14336, 24, seed=2)
     xt = f64(w.x[:, cols]).T.copy()
     compare_nv(u8(o.codes_col[cols]), u8(o.scales_col[cols]), rht.rht_rowwise(xt, mask), xt,

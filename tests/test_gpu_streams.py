@@ -16,13 +16,16 @@ pytestmark = pytest.mark.gpu
 
 def run_all(x, q8, s128, codes, e8, off, groups, amax):
     """One call of each entry point; returns every output tensor."""
-    mask = mxq.mxq_rht_signs(4)
     out = []
     o = mxq.mxq_quantize(x, "mxfp4", "both")
     out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col]
     out.append(mxq.mxq_dequantize(o.codes_row, o.scales_row, "mxfp4", out_dtype=torch.bfloat16))
-    o = mxq.mxq_rht_quantize(x, mask, "mxfp4", "both")
+    o = mxq.mxq_rht_quantize(x, 4, "mxfp4", "both")
     out += [o.codes_row, o.scales_row, o.codes_col, o.scales_col]
+    o = mxq.mxq_rht_quantize(x, 4, "nvfp4", "col")  # amax of the transform computed first
+    out += [o.codes_col, o.scales_col, o.tensor_scale]
+    o = mxq.mxq_quantize(x, "nvfp4", "row")  # tensor amax computed first
+    out += [o.codes_row, o.scales_row, o.tensor_scale]
     a = mxq.mxq_amax(x)
     out.append(a)
     o = mxq.mxq_quantize(x, "nvfp4", "row", "sr", sr_seed=7, sr_offset=3, amax=amax)
