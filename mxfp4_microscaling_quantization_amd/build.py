@@ -1,4 +1,5 @@
-"""Build libmxq.so (all HIP sources under csrc/) for gfx950, in the package directory.
+"""Build libmxq.so (all HIP sources under csrc/) for gfx950, in the package directory,
+and the benchmark's streaming reference library libmxq_stream.so (csrc_bench/).
 
 Usage: python -m mxfp4_microscaling_quantization_amd.build
 """
@@ -13,6 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmxq.so")
+STREAM_LIB = os.path.join(PKG, "libmxq_stream.so")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -38,14 +40,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = True) -> str:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
+def _compile(srcs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    _compile(sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip"))), LIB, verbose)
+    _compile(sorted(glob.glob(os.path.join(PKG, "csrc_bench", "*.hip"))), STREAM_LIB, verbose)
     return LIB
 
 
