@@ -30,8 +30,13 @@ Parity status per function (what pins it is in tests/test_oracle_*.py):
                        force over ragged expert segments)
   rht.*                pinned (scipy Hadamard, orthogonality, inverse, norms)
   nvfp4.*              pinned (Fraction brute force, torch E4M3 cast, invariants)
-  philox.philox4x32_10 pinned against rocRAND's independent Philox4x32-10 header
-                       when hipcc is present (skipped otherwise); statistical tests
+  philox.philox4x32_10 pinned against the published known-answer vectors of
+                       Philox4x32-10 (tests/golden/philox_kat.json) and against
+                       rocRAND's independent Philox4x32-10 header when hipcc is
+                       present (skipped otherwise); statistical tests
+  philox.element_r16_halves  pinned against rocRAND's word stream (half n mod 2 of
+                       word n/2), a hand-worked vector from the known-answer words,
+                       and uniformity / unbiased-rounding statistics
   rht.sign_mask_from_seed  parity unpinned: the seed-to-signs mapping is a
                        definition made here (the pages only say "random signs").
 """

@@ -16,6 +16,13 @@ a tensor uses the 32-bit word (n mod 4) of Philox(counter = (floor(n/4) low 32
 bits, floor(n/4) high 32 bits, 0, 0), key = (seed low 32, seed high 32)); n is
 the caller's base offset plus the element's row-major index in the tensor being
 quantised. Stochastic rounding uses the top 16 bits of that word.
+
+Opt-in cheaper stream (16-bit halves; a definition made here, not in the pages):
+element n uses the 16-bit half (n mod 2) -- the low half for even n -- of word
+((n mod 8) div 2) of Philox(counter = (floor(n/8) low, floor(n/8) high, 0, 0), same
+key), so one generator call serves eight consecutive elements. Equivalently, it is
+half (n mod 2) of word (n div 2) of the default element stream. It trades the
+per-element 32-bit word for a 16-bit value, which is all the rounding rule reads.
 """
 from __future__ import annotations
 
@@ -67,3 +74,23 @@ def tensor_r16(rows: int, cols: int, seed: int, offset: int = 0) -> np.ndarray:
     """r16 for every element of a row-major [rows, cols] tensor, n = offset + r*cols + c."""
     n = np.uint64(offset) + np.arange(rows * cols, dtype=np.uint64)
     return element_r16(n, seed).reshape(rows, cols)
+
+
+def element_r16_halves(n: np.ndarray, seed: int) -> np.ndarray:
+    """The 16-bit value of each element index n in the opt-in halves stream."""
+    n = np.asarray(n, dtype=np.uint64)
+    flat = n.reshape(-1)
+    ctr = flat >> np.uint64(3)
+    counters = np.zeros((flat.size, 4), dtype=np.uint32)
+    counters[:, 0] = (ctr & MASK32).astype(np.uint32)
+    counters[:, 1] = (ctr >> np.uint64(32)).astype(np.uint32)
+    w = philox4x32_10(counters, seed)
+    word = w[np.arange(flat.size), ((flat & np.uint64(7)) >> np.uint64(1)).astype(np.int64)]
+    half = (flat & np.uint64(1)).astype(np.uint32)
+    return ((word >> (np.uint32(16) * half)) & np.uint32(0xFFFF)).astype(np.uint16).reshape(n.shape)
+
+
+def tensor_r16_halves(rows: int, cols: int, seed: int, offset: int = 0) -> np.ndarray:
+    """Halves-stream values for a row-major [rows, cols] tensor, n = offset + r*cols + c."""
+    n = np.uint64(offset) + np.arange(rows * cols, dtype=np.uint64)
+    return element_r16_halves(n, seed).reshape(rows, cols)

@@ -165,15 +165,16 @@ def test_dequantize_single_rounding():
         assert ref >= 0
 
 
+@pytest.mark.parametrize("stream", ["words", "halves"])
 @pytest.mark.parametrize("which", ["nvfp4", "mxfp4"])
-def test_stochastic_rounding_statistics(which):
+def test_stochastic_rounding_statistics(which, stream):
     rng = np.random.default_rng(7)
     # one block repeated: fixed scales, many random draws
     row = np.concatenate([[6.0], rng.uniform(-6, 6, 15)])
     row = torch.from_numpy(row).to(torch.bfloat16).double().numpy()
     reps = 4096
     x = np.tile(row, (reps, 2))  # [reps, 32]
-    r16 = philox.tensor_r16(reps, 32, seed=7)
+    r16 = (philox.tensor_r16 if stream == "words" else philox.tensor_r16_halves)(reps, 32, seed=7)
     if which == "nvfp4":
         p, sb, st = nvfp4.nvfp4_quantize_rowwise(x, r16=r16)
         v = nvfp4.nvfp4_dequantize_values(p, sb, st)
