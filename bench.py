@@ -181,6 +181,28 @@ def build_step(wl, dev, sets: int):
 # ---------------------------------------------------------------------------
 # timing helpers
 
+_busy = None
+
+
+def keep_busy(dev, seconds: float = 0.25) -> None:
+    """Keeps the GPU busy for `seconds` with a compute-only kernel (no memory traffic),
+    so the measurement that follows does not start on a clock that dropped while the
+    host prepared its buffers (a few hundred ms idle lowers it; kernels bound by the
+    vector ALU then run up to 25 % slower)."""
+    import torch
+
+    global _busy
+    L = stream_lib()
+    if _busy is None:
+        _busy = torch.empty(2048, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            L.mxq_valu_probe(_busy.data_ptr(), 2048, 256, 0, st)
+        torch.cuda.synchronize()
+
+
 def avg_launch_us(fn, sets: int, reps: int) -> float:
     """Average duration of `reps` back-to-back launches rotating over the buffer sets,
     between two events on the stream the kernels run on (torch's current stream)."""
@@ -262,6 +284,7 @@ def stream_mix_reference(dev, read_bytes: int, rd: int, wr: int, flags: int, rep
 
     for k in range(sets):
         fn(k)
+    keep_busy(dev)
     us = avg_launch_us(fn, sets, reps)
     nbytes = units * (rd + wr)
     out = figures(us, nbytes, units)
@@ -292,6 +315,7 @@ def tile_pattern_reference(dev, rows: int, cols: int, tile_rows: int, reps: int,
 
     for k in range(sets):
         fn(k)
+    keep_busy(dev)
     us = avg_launch_us(fn, sets, reps)
     n = rows * cols
     out = figures(us, 2 * n + 2 * (n // 2 + n // 32), n)
@@ -312,6 +336,7 @@ def valu_probe(dev, reps: int = 5) -> dict:
     out = torch.empty(blocks, dtype=torch.int32, device=dev)
     st = torch.cuda.current_stream().cuda_stream
     res = {}
+    keep_busy(dev)
     for kind, name in ((0, "v_add_u32"), (1, "v_bitop3_b32"), (2, "v_mad_u64_u32")):
         fn = lambda k: L.mxq_valu_probe(out.data_ptr(), blocks, iters, kind, st)  # noqa: E731
         fn(0)
@@ -328,7 +353,7 @@ def valu_probe(dev, reps: int = 5) -> dict:
 # ---------------------------------------------------------------------------
 # config 1, the rows beyond the step, the ablation
 
-def config1_report(wl, dev, reps: int) -> list:
+def config1_report(wl, dev, reps: int, graph: bool = True) -> list:
     """1024 x 4096 (10.6 MB): 64 rotating buffer sets, eager launches and the same
     launches replayed from a captured HIP graph (device time without the host's
     per-call cost)."""
@@ -371,17 +396,19 @@ def config1_report(wl, dev, reps: int) -> list:
     for name, fn in (("mxfp4_quantize", qfn), ("mxfp4_dequantize", dfn)):
         for k in range(n):
             fn(k)
+        keep_busy(dev)
         r = {"config": "cfg1", "kernel": name, "shape": f"{R}x{C}", "launch": "eager"}
         r.update(figures(avg_launch_us(fn, n, reps), mx_bytes(N), N))
         out.append(r)
-        r = {"config": "cfg1", "kernel": name, "shape": f"{R}x{C}", "launch": "hip_graph"}
-        r.update(figures(graph_us(fn), mx_bytes(N), N))
-        out.append(r)
+        if graph:
+            r = {"config": "cfg1", "kernel": name, "shape": f"{R}x{C}", "launch": "hip_graph"}
+            r.update(figures(graph_us(fn), mx_bytes(N), N))
+            out.append(r)
     del xs, qs, ys
     return out
 
 
-def extra_rows(wl, dev, reps: int) -> tuple[dict, dict]:
+def extra_rows(wl, dev, reps: int, traffic: dict) -> tuple[dict, dict]:
     """The rows beyond the step, each at its own workload with rotating input copies:
     NVFP4 amax + quantise as one call (the amax computed by the call), 16x16-scaled
     NVFP4 of a 14336 x 4096 FFN weight (both outputs), RHT + NVFP4 column-wise and
@@ -398,9 +425,13 @@ def extra_rows(wl, dev, reps: int) -> tuple[dict, dict]:
     def row(name, cfg, shape, fn, n, nbytes, elements, note):
         for k in range(n):
             fn(k)
+        keep_busy(dev)
         us = avg_launch_us(fn, n, reps)
         r = {"config": cfg, "shape": shape, "workload": note}
         r.update(figures(us, nbytes, elements))
+        t = traffic.get(name, {}).get("hbm_bytes")
+        r["hbm_traffic_bytes"] = t
+        r["traffic_ratio"] = round(t / nbytes, 4) if t else None
         rows[name] = r
         print(f"[next] {name:28s} {us:9.2f} us  {r['GB_s']:8.1f} GB/s  {100 * r['frac_hbm_peak']:5.1f}%",
               file=sys.stderr, flush=True)
@@ -416,7 +447,12 @@ def extra_rows(wl, dev, reps: int) -> tuple[dict, dict]:
         lambda k: mxq.mxq_quantize(x5[k], "nvfp4", "row", out=o5[k]), n, nv_bytes(N5), N5,
         "amax pass + quantise pass in one call (NULL amax); bytes = the quantiser's in+out, "
         "so the two-pass ceiling is 2.5625 / 4.5625 of the HBM peak")
-    del x5, o5
+    a5 = [mxq.mxq_amax(v) for v in x5]
+    row("nvfp4_quantize_sr16", "cfg5", f"{R5}x{C5}",
+        lambda k: mxq.mxq_quantize(x5[k], "nvfp4", "row", "sr16", sr_seed=wl["cfg5"].sr_seed, amax=a5[k],
+                                   out=o5[k]), n, nv_bytes(N5), N5,
+        "NVFP4 stochastic rounding, opt-in 16-bit-halves random stream (one Philox call per 8 elements)")
+    del x5, o5, a5
     # 16x16 NVFP4 of an FFN weight
     wt = workloads.outlier_normal(14336, 4096, 5)
     ws = [wt.to(dev) for _ in range(n)]
@@ -446,6 +482,9 @@ def extra_rows(wl, dev, reps: int) -> tuple[dict, dict]:
     row("mxfp4_quantize_sr", "cfg4", f"{R4}x{C4}",
         lambda k: mxq.mxq_quantize(x4[k], "mxfp4", "row", "sr", sr_seed=7, out=sq[k]), n, mx_bytes(N4), N4,
         "row-wise MXFP4, Philox stochastic rounding (gradients)")
+    row("mxfp4_quantize_sr16", "cfg4", f"{R4}x{C4}",
+        lambda k: mxq.mxq_quantize(x4[k], "mxfp4", "row", "sr16", sr_seed=7, out=sq[k]), n, mx_bytes(N4), N4,
+        "row-wise MXFP4, stochastic rounding with the opt-in 16-bit-halves stream")
     rcol = [(torch.empty((C4, R4 // 2), dtype=torch.uint8, device=dev),
              torch.empty((C4, R4 // 32), dtype=torch.uint8, device=dev)) for _ in range(n)]
     row("mxfp4_rowcol_no_rht", "cfg4", f"{R4}x{C4}",
@@ -640,6 +679,7 @@ def main() -> int:
     ap.add_argument("--cpu-procs", type=int, default=0, help="oracle pool size (0: the affinity mask, at most 16)")
     ap.add_argument("--no-next", action="store_true", help="skip the rows beyond the step and the ablation")
     ap.add_argument("--no-refs", action="store_true", help="skip the streaming references and the VALU probe")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing of configuration 1")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one MI355X: the quantisation kernels need no collectives and this "
@@ -753,7 +793,7 @@ def main() -> int:
     if valu_ref:
         valu["probe"] = valu_ref
 
-    config1 = config1_report(wl, dev, args.kernel_reps)
+    config1 = config1_report(wl, dev, args.kernel_reps, graph=not args.no_graph)
     for r in config1:
         print(f"[cfg1]  {r['kernel']:18s} {r['launch']:9s} {r['us']:8.2f} us  {100 * r['frac_hbm_peak']:5.1f}%",
               file=sys.stderr, flush=True)
@@ -762,7 +802,7 @@ def main() -> int:
     if not args.no_next:
         del kernels
         torch.cuda.empty_cache()
-        nxt, abl = extra_rows(wl, dev, args.kernel_reps)
+        nxt, abl = extra_rows(wl, dev, args.kernel_reps, traffic)
 
     line = {
         "metric": "quantize/convert GB/s (in+out bytes) and % of MI355X HBM peak, per kernel",

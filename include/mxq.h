@@ -67,7 +67,7 @@ typedef enum {
 
 typedef enum { MXQ_BF16 = 0, MXQ_F32 = 1 } mxq_dtype;
 typedef enum { MXQ_MXFP4 = 0, MXQ_NVFP4 = 1, MXQ_NVFP4_2D = 2 } mxq_format;
-typedef enum { MXQ_RNE = 0, MXQ_SR = 1 } mxq_round;
+typedef enum { MXQ_RNE = 0, MXQ_SR = 1, MXQ_SR16 = 2 } mxq_round;
 typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
 
 /*
@@ -90,13 +90,19 @@ typedef enum { MXQ_ROWWISE = 1, MXQ_COLWISE = 2, MXQ_BOTH = 3 } mxq_axis;
  *   (column-wise): the column-wise output is exactly the transpose of the row-wise
  *   one, so one quantisation serves W and W^T, and mxq_dequantize reads it as
  *   NVFP4. rows % 16 == 0 and cols % 16 == 0 for any axis; round to nearest even
- *   only (MXQ_SR returns MXQ_EUNSUPPORTED).
+ *   only (MXQ_SR and MXQ_SR16 return MXQ_EUNSUPPORTED).
  * Stochastic rounding (rnd == MXQ_SR; [NVFP4] section 2B, gradients): element n
  *   (n = sr_offset + its row-major index in the tensor quantised; for column-wise
  *   outputs the index in the transpose) draws the 32-bit word n mod 4 of
  *   Philox4x32-10(counter = (n/4 lo, n/4 hi, 0, 0), key = (seed lo, seed hi)); with
  *   r its top 16 bits, lo the grid value at or below y = |x|/scale and step the gap
  *   to the next, y rounds up iff y > lo + step (r + 1/2) / 2^16; y >= 6 gives 6.
+ * Stochastic rounding, halves stream (rnd == MXQ_SR16, opt-in; a cheaper random
+ *   stream defined by this library, not by the pages): the same rule with r the
+ *   16-bit half (n mod 2), low half for even n, of word (n mod 8) / 2 of
+ *   Philox4x32-10(counter = (n/8 lo, n/8 hi, 0, 0), same key), i.e. half n mod 2 of
+ *   word n / 2 of the default stream: one generator call serves eight elements.
+ *   Results differ from MXQ_SR. sr_offset % 8 == 0 (else MXQ_EALIGN).
  *
  * x            device, bf16 or fp32 [rows, ldx]; 16-byte aligned, ldx*sizeof a
  *              multiple of 16 bytes.

@@ -40,14 +40,14 @@ uint32_t philox_word0(uint64_t counter, uint64_t seed) {
 
 // Shared checks of the quantise entry points.
 mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
-                          mxq_format fmt, mxq_axis axis, mxq_round rnd, const uint8_t* codes_row,
+                          mxq_format fmt, mxq_axis axis, mxq_round rnd, uint64_t sr_offset, const uint8_t* codes_row,
                           const uint8_t* scales_row, const uint8_t* codes_col,
                           const uint8_t* scales_col, const float* amax, const float* tensor_scale) {
   if (dt != MXQ_BF16 && dt != MXQ_F32) return MXQ_EINVAL;
   if (fmt != MXQ_MXFP4 && fmt != MXQ_NVFP4 && fmt != MXQ_NVFP4_2D) return MXQ_EINVAL;
   if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE && axis != MXQ_BOTH) return MXQ_EINVAL;
-  if (rnd != MXQ_RNE && rnd != MXQ_SR) return MXQ_EINVAL;
-  if (fmt == MXQ_NVFP4_2D && rnd == MXQ_SR) return MXQ_EUNSUPPORTED;
+  if (rnd != MXQ_RNE && rnd != MXQ_SR && rnd != MXQ_SR16) return MXQ_EINVAL;
+  if (fmt == MXQ_NVFP4_2D && rnd != MXQ_RNE) return MXQ_EUNSUPPORTED;
   if (rows < 0 || cols < 0) return MXQ_EINVAL;
   if (rows == 0) return MXQ_OK;
   if (!x) return MXQ_EINVAL;
@@ -68,6 +68,9 @@ mxq_status check_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t col
   if (col && (!aligned(codes_col, 16) || !aligned(scales_col, 4))) return MXQ_EALIGN;
   if (fmt != MXQ_MXFP4 && ((amax && !aligned(amax, 4)) || (tensor_scale && !aligned(tensor_scale, 4))))
     return MXQ_EALIGN;
+  // the halves stream serves eight elements per generator call from element offsets
+  // that are multiples of 8
+  if (rnd == MXQ_SR16 && sr_offset % 8) return MXQ_EALIGN;
   return MXQ_OK;
 }
 
@@ -76,7 +79,7 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
                          uint64_t sr_seed, uint64_t sr_offset, uint8_t* codes_row,
                          uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                          const float* amax, float* tensor_scale, void* stream) {
-  mxq_status s = check_quantize(x, dt, rows, cols, ldx, fmt, axis, rnd, codes_row, scales_row,
+  mxq_status s = check_quantize(x, dt, rows, cols, ldx, fmt, axis, rnd, sr_offset, codes_row, scales_row,
                                 codes_col, scales_col, amax, tensor_scale);
   if (s != MXQ_OK || rows == 0) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -124,7 +127,7 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
     a.cols = cols;
     a.dtype = dt;
     a.fmt = fmt == MXQ_MXFP4 ? kMX : kNV;
-    a.sr = rnd == MXQ_SR;
+    a.sr = (int)rnd;  // 0 nearest even, 1 word stream, 2 halves stream
     a.rht = rht;
     a.sign_mask = sign_mask & 0xFFFFu;
     a.sr_seed = sr_seed;
@@ -143,7 +146,7 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
   a.cols = cols;
   a.dtype = dt;
   a.fmt = fmt == MXQ_MXFP4 ? kMX : kNV;
-  a.sr = rnd == MXQ_SR;
+  a.sr = (int)rnd;  // 0 nearest even, 1 word stream, 2 halves stream
   a.rht = rht;
   a.want_row = axis & MXQ_ROWWISE;
   a.want_col = true;

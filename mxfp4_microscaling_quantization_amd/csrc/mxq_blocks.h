@@ -157,10 +157,6 @@ __device__ __forceinline__ float absmax8(const float* v) {
   return m;
 }
 
-__device__ __forceinline__ void sr_words8(uint64_t n, uint64_t seed, uint32_t u[8]) {
-  philox_words<8>(n, seed, u);
-}
-
 // E8M0 byte of a block from its amax bits (exponent field ea of max|z|), where the
 // values z are the real values times 2^kShift (kShift = 2 when the Hadamard
 // transform's 1/4 is still to be applied). 255: NaN or Inf in the block.
@@ -170,8 +166,22 @@ __device__ __forceinline__ uint32_t mx_byte(uint32_t amax_bits) {
   return ea >= 255u ? 255u : (ea > 2u + kShift ? ea - 2u - kShift : 0u);
 }
 
+// MXFP4 stochastic rounding of 8 values that are bf16 numbers (no transform) by the
+// hardware conversion: for such values the position F inside an interval is a whole
+// number of units unless |x| / 2^E < 2^-16, where F < 128 and only r <= 1 can meet
+// a threshold: chunks holding such an r return false and take the carry path.
+__device__ __forceinline__ bool mx_sr_hw8(const float v[8], const uint32_t u[8], uint32_t b, uint32_t& packed) {
+  if (min_u8(u) < 0x20000u) return false;
+  uint32_t sd[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sd[i] = sr_hw_seed(u[i], kSrHwExact);
+  packed = fp4x8_sr_hw(v, sd, e8m0_operand(b));
+  return true;
+}
+
 // MXFP4: 8 values of one lane (a quarter of a 32-block) -> 8 codes, block byte.
-template <bool SR, int kShift>
+// kBf16: the values are bf16 numbers (stochastic rounding may use the hardware).
+template <bool SR, int kShift, bool kBf16 = false>
 __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t u[8],
                                                uint32_t& byte) {
   float am = absmax8(v);
@@ -180,6 +190,9 @@ __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t 
   byte = mx_byte<kShift>(as_u(am));
   const uint32_t b = min(byte, 252u);
   uint32_t packed = 0;
+  if constexpr (SR && kBf16 && kShift == 0) {
+    if (mx_sr_hw8(v, u, b, packed)) return byte == 255u ? 0u : packed;
+  }
   if constexpr (SR) {
     const float inv = as_f((254u - b - kShift) << 23);  // 2^-(E + kShift), exact
     // y is exact; only the rounding of y + 1 (half a unit of F) can mislead the
@@ -187,7 +200,12 @@ __device__ __forceinline__ uint32_t mx_encode8(const float v[8], const uint32_t 
     float q[8];
     uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_carry<1>(fabsf(v[i]) * inv, u[i], low), v[i]);
+    for (int i = 0; i < 8; i += 2) {
+      float q0, q1;
+      e2m1_sr_carry2<1>(fabsf(v[i]) * inv, fabsf(v[i + 1]) * inv, u[i], u[i + 1], low, q0, q1);
+      q[i] = with_sign_of(q0, v[i]);
+      q[i + 1] = with_sign_of(q1, v[i + 1]);
+    }
     if (low < 2u) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_value(fabsf(v[i]) * inv, u[i]), v[i]);

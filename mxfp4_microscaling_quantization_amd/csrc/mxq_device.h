@@ -109,14 +109,6 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
   return b >= 0x3F800000u ? hi : lo;
 }
 
-// Largest E2M1 magnitude code whose value is <= y (round toward zero; y >= 0).
-__device__ __forceinline__ uint32_t e2m1_floor(float y) {
-  const uint32_t b = as_u(y);
-  const uint32_t hi = min(b >> 22, 259u) - 252u;
-  const uint32_t lo = y >= 0.5f ? 1u : 0u;
-  return b >= 0x3F800000u ? hi : lo;
-}
-
 // E2M1 magnitude of a code 0..7 as fp32 (0, .5, 1, 1.5, 2, 3, 4, 6).
 __device__ __forceinline__ float e2m1_value(uint32_t m) {
   const uint32_t normal = (m << 22) + 0x3F000000u;  // m >= 2: exponent/mantissa fields
@@ -124,11 +116,9 @@ __device__ __forceinline__ float e2m1_value(uint32_t m) {
 }
 
 // ---------------------------------------------------------------------------
-// E4M3 ("fn") magnitude code k (0..126) -> fp32 value, and nearest-even encoding.
-__device__ __forceinline__ float e4m3_value(uint32_t k) {
-  const uint32_t e = k >> 3, m = k & 7u;
-  return e ? as_f(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;  // m * 2^-9
-}
+// E4M3 ("fn") magnitude code k (0..126) -> fp32 value (gfx950's FP8 conversion
+// decodes the OCP E4M3 byte exactly, subnormals included), and nearest-even encoding.
+__device__ __forceinline__ float e4m3_value(uint32_t k) { return __builtin_amdgcn_cvt_f32_fp8((int)k, 0); }
 
 // E4M3 magnitude code of RNE(v) for a finite v >= 0 (exact input), saturating at 448.
 __device__ __forceinline__ uint32_t e4m3_rne(float v) {
@@ -206,6 +196,50 @@ __device__ __forceinline__ void philox_words(uint64_t n, uint64_t seed, uint32_t
   }
 }
 
+// Random values of elements n .. n+K-1 in the 16-bit-halves stream (n and K
+// multiples of 8): element m takes half (m mod 2), the low half for even m, of word
+// (m mod 8) / 2 of Philox4x32-10(counter = (m/8 lo, m/8 hi, 0, 0)), so one call
+// serves eight elements. Each value is returned in bits 16..31 of u[i], the bits
+// the stochastic rounding reads (bits 0..15 are not used).
+template <int K>
+__device__ __forceinline__ void philox_halves(uint64_t n, uint64_t seed, uint32_t* u) {
+  const uint64_t c0 = n >> 3;
+#pragma unroll
+  for (int i = 0; i < K / 8; ++i) {
+    const uint64_t ctr = c0 + i;
+    const u32x4 a = philox4x32_10(u32x4{(uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u}, (uint32_t)seed,
+                                  (uint32_t)(seed >> 32));
+    u[8 * i + 0] = a.x << 16; u[8 * i + 1] = a.x;
+    u[8 * i + 2] = a.y << 16; u[8 * i + 3] = a.y;
+    u[8 * i + 4] = a.z << 16; u[8 * i + 5] = a.z;
+    u[8 * i + 6] = a.w << 16; u[8 * i + 7] = a.w;
+  }
+}
+
+// The four words serving elements n .. n+7 of the halves stream (n a multiple of
+// 8), and their expansion into per-element values as philox_halves returns them.
+__device__ __forceinline__ u32x4 philox_halves_words(uint64_t n, uint64_t seed) {
+  const uint64_t ctr = n >> 3;
+  return philox4x32_10(u32x4{(uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u}, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+__device__ __forceinline__ void expand_halves(const u32x4& a, uint32_t* u) {
+  u[0] = a.x << 16; u[1] = a.x;
+  u[2] = a.y << 16; u[3] = a.y;
+  u[4] = a.z << 16; u[5] = a.z;
+  u[6] = a.w << 16; u[7] = a.w;
+}
+
+// The random values of a stochastic-rounding mode: kSrWords (one Philox word per
+// element, the top 16 bits used) or kSrHalves (one 16-bit half per element).
+enum SrStream : int { kRne = 0, kSrWords = 1, kSrHalves = 2 };
+
+template <int SR, int K>
+__device__ __forceinline__ void sr_values(uint64_t n, uint64_t seed, uint32_t* u) {
+  if constexpr (SR == kSrWords) philox_words<K>(n, seed, u);
+  else if constexpr (SR == kSrHalves) philox_halves<K>(n, seed, u);
+}
+
 // Word of one element n (any n).
 __device__ __forceinline__ uint32_t philox_word(uint64_t n, uint64_t seed) {
   const u32x4 w = philox_words4(n & ~3ull, seed);
@@ -251,7 +285,6 @@ __device__ __forceinline__ float e2m1_sr_value(float y, uint32_t u) {
   return fminf(y > thr ? lo + step : lo, 6.0f);
 }
 
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) { return e2m1_rne(e2m1_sr_value(y, u)); }
 
 // The same stochastic rounding decided by a carry. Adding 1 to y < 1 moves the grid
 // 0, 0.5, 1 onto 1, 1.5, 2, so every grid interval is one fp32 mantissa bit wide.
@@ -278,6 +311,43 @@ __device__ __forceinline__ float e2m1_sr_carry(float y, uint32_t u, uint32_t& lo
   asm("v_sad_u32 %0, %1, %2, %3" : "=v"(s) : "v"(as_u(y + off)), "v"(r64), "v"(0x3FFFC0u + 31u + K));
   low = min(low, s & 0x3FFFFFu);
   return as_f(s & 0xFFC00000u) - off;
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic rounding by gfx950's scaled stochastic FP4 conversion
+// (v_cvt_scalef32_sr_pk_fp4_f32), one value per instruction in its first slot (the
+// second slot reads overlapping seed bits, so it cannot serve an independent
+// element). Characterised on the chip over every E2M1 interval, both signs and
+// power-of-two scales: with F the position of y = x / scale inside its E2M1
+// interval in units of 2^-22 of the interval, rounded down, the conversion rounds
+// |y| up iff F + (seed >> 10) >= 2^22; values of 6 and more give 6; the sign is
+// kept. The rule of this library rounds up iff the exact position exceeds 64 r + 32
+// units (r the element's 16 random bits). A seed with seed >> 10 = 2^22 - 64 r - c,
+// i.e. (~r << 16) | (64 - c) << 10, makes the conversion round up iff F >= 64 r + c.
+// u carries r in bits 16..31.
+__device__ __forceinline__ uint32_t sr_hw_seed(uint32_t u, uint32_t low) { return (~u & 0xFFFF0000u) | low; }
+constexpr uint32_t kSrHwExact = 31u << 10;  // c = 33: F >= 64 r + 33, the rule for integer F
+
+// 8 signed values, each converted stochastically with its own seed under one scale:
+// codes packed two per byte, element 2j in the low nibble. Every conversion writes
+// byte 0 of its own result (the value's code in bits 0-3, the code of +0 in bits
+// 4-7) and only that byte is used: chaining the byte selects through one register
+// leaves the other bytes to the register allocator, which does not keep the chain
+// in one register. v_perm_b32 then gathers the bytes.
+__device__ __forceinline__ uint32_t fp4x8_sr_hw(const float* v, const uint32_t* seed, float scale) {
+  uint32_t r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f32x2_t{v[i], 0.0f}, seed[i], scale, 0);
+  // bytes (r_a.b0, r_b.b0, 0, 0) of two results
+  constexpr uint32_t kLow2 = 0x0C0C0400u;
+  const uint32_t e = __builtin_amdgcn_perm(r[2], r[0], kLow2) | (__builtin_amdgcn_perm(r[6], r[4], kLow2) << 16);
+  const uint32_t o = __builtin_amdgcn_perm(r[3], r[1], kLow2) | (__builtin_amdgcn_perm(r[7], r[5], kLow2) << 16);
+  return e | (o << 4);
+}
+
+// The smallest random value of 8 elements (r in bits 16..31 of u), as u bits.
+__device__ __forceinline__ uint32_t min_u8(const uint32_t* u) {
+  return min(min(min(u[0], u[1]), min(u[2], u[3])), min(min(u[4], u[5]), min(u[6], u[7])));
 }
 
 // ---------------------------------------------------------------------------
@@ -374,133 +444,100 @@ __device__ __forceinline__ NvTensor nv_tensor_load(const float* src, bool st_giv
   return st_given ? nv_tensor_from_st(*src) : nv_tensor(*src);
 }
 
-// Exact E4M3 (nearest even, saturating) code of a_n / (6 st_n); a_n >= 0 exact.
-__device__ __forceinline__ uint32_t nv_block_scale(float a_n, float st_n) {
-  const float q = a_n * __builtin_amdgcn_rcpf(6.0f * st_n);
-  uint32_t k = e4m3_rne(q);
-  bool moved = false;
-  if (k < 126u) {
-    const float mu6 = 3.0f * (e4m3_value(k) + e4m3_value(k + 1u));  // 6 * midpoint, exact
-    const float r = fmaf(mu6, st_n, -a_n);
-    if (r < 0.0f || (r == 0.0f && ((k + 1u) & 1u) == 0u)) {
-      k += 1u;
-      moved = true;
-    }
-  }
-  if (!moved && k > 0u) {
-    const float mu6 = 3.0f * (e4m3_value(k - 1u) + e4m3_value(k));
-    const float r = fmaf(mu6, st_n, -a_n);
-    if (r > 0.0f || (r == 0.0f && ((k - 1u) & 1u) == 0u)) k -= 1u;
-  }
-  return k;
+// The midpoint decision of one element whose two roundings differ (lo, hi: the
+// E2M1 codes with sign, from y (1 - 2^-20) and y (1 + 2^-20)): with m the
+// midpoint of their magnitudes, the sign of m s_b s_t - |x| (exact: m s_b has at
+// most 7 significant bits) picks lo, hi or, on an exact tie, the even one. xs and
+// sts are |x| and s_t, both normalised by 2^-et when s_t is tiny.
+__device__ __forceinline__ uint32_t nv_midpoint_pick(uint32_t lo, uint32_t hi, float xs, float sb, float sts) {
+  const f32x2_t g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((lo & 7u) | ((hi & 7u) << 4), 1.0f, 0);
+  const float m = 0.5f * (g.x + g.y);
+  const float d = fmaf(m * sb, sts, -xs);  // > 0: the quotient is below m
+  return d > 0.0f ? lo : (d < 0.0f ? hi : ((lo & 1u) ? hi : lo));
 }
 
-// y_a is within a few ulps of a value with at most 3 significant bits (every
-// E2M1 grid value and rounding midpoint is one), at or above 0.2.
-__device__ __forceinline__ bool near_3bit(float y_a) {
-  const uint32_t b = as_u(y_a);
-  return b >= 0x3E4CCCCDu && ((b + 64u) & 0x1FFFFFu) <= 128u;
-}
-
-// Exact nearest-even E2M1 code of x_n / (sb * st_n) by threshold tests.
-__device__ __forceinline__ uint32_t nv_code_exact(float x_n, float sb, float st_n) {
-  uint32_t c = 0;
-  c += fmaf(0.25f * sb, st_n, -x_n) < 0.0f;
-  c += fmaf(0.75f * sb, st_n, -x_n) <= 0.0f;
-  c += fmaf(1.25f * sb, st_n, -x_n) < 0.0f;
-  c += fmaf(1.75f * sb, st_n, -x_n) <= 0.0f;
-  c += fmaf(2.5f * sb, st_n, -x_n) < 0.0f;
-  c += fmaf(3.5f * sb, st_n, -x_n) <= 0.0f;
-  c += fmaf(5.0f * sb, st_n, -x_n) < 0.0f;
-  return c;
-}
-
-// Exact largest code whose value is <= x_n / (sb * st_n).
-__device__ __forceinline__ uint32_t nv_floor_exact(float x_n, float sb, float st_n) {
-  uint32_t c = 0;
+// Codes of 8 values rounded twice (clo, chi differ where a midpoint lies between):
+// the differing nibbles are decided exactly, one per iteration (such elements are
+// rare but can be structural, e.g. bf16 data whose exact quotients hit midpoints up
+// to the rounding of s_t). |v[j]| is taken times 2^sh, the domain of `sts`.
+__device__ __forceinline__ uint32_t nv_resolve8(uint32_t clo, uint32_t chi, const float* v, int sh, float sb,
+                                                float sts) {
+  uint32_t out = clo;
+  uint32_t pending = clo ^ chi;
+  while (pending) {
+    const uint32_t bit = (uint32_t)__builtin_ctz(pending) & ~3u;  // bit offset of the nibble
+    pending &= ~(0xFu << bit);
+    float xv = v[0];
 #pragma unroll
-  for (uint32_t m = 1; m < 8; ++m) c += fmaf(e2m1_value(m) * sb, st_n, -x_n) <= 0.0f;
-  return c;
-}
-
-// NVFP4 element code (magnitude) with round-to-nearest-even.
-__device__ __forceinline__ uint32_t nv_code_rne(float x_n, float sb, float inv, float st_n) {
-  const float y = x_n * inv;
-  const uint32_t c = e2m1_rne(y);
-  return near_3bit(y) ? nv_code_exact(x_n, sb, st_n) : c;
-}
-
-// NVFP4 element code (magnitude) with stochastic rounding (word u).
-__device__ __forceinline__ uint32_t nv_code_sr(float x_n, float sb, float inv, float st_n,
-                                               uint32_t u) {
-  const float y = x_n * inv;
-  uint32_t lo = e2m1_floor(y);
-  if (near_3bit(y)) lo = nv_floor_exact(x_n, sb, st_n);
-  if (lo >= 7u) return 7u;
-  const float vlo = e2m1_value(lo);
-  const float step = e2m1_value(lo + 1u) - vlo;
-  const float thr = vlo + step * ((float)(u >> 16) + 0.5f) * (1.0f / 65536.0f);
-  return fmaf(thr * sb, st_n, -x_n) < 0.0f ? lo + 1u : lo;
+    for (int j = 1; j < 8; ++j) xv = bit == 4u * j ? v[j] : xv;
+    const float xs = ldexpf(fabsf(xv), sh);
+    const uint32_t c = nv_midpoint_pick((clo >> bit) & 0xFu, (chi >> bit) & 0xFu, xs, sb, sts);
+    out = (out & ~(0xFu << bit)) | (c << bit);
+  }
+  return out;
 }
 
 // Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1,
 // nearest even. The quotient y = |x| / (s_b s_t) is approximated in fp32 to a few
 // ulp and rounded twice by the hardware conversion, at y (1 - 2^-20) and
 // y (1 + 2^-20). Equal codes bracket the exact quotient and are the answer; where
-// they differ a single rounding midpoint m lies between them, and the sign of
-// fma(m s_b, s_t, -|x|) (exact) picks the lower code, the upper one, or on an
-// exact tie the even one. When s_t < 2^-80 the same tests run on values
-// normalised by 2^-et.
+// they differ a single rounding midpoint lies between them and nv_resolve8 decides
+// exactly. When s_t < 2^-80 the same steps run on values normalised by 2^-et (a
+// uniform branch: the common case carries no per-element selection).
 __device__ __forceinline__ uint32_t nv_codes8_rne(const float* v, const NvTensor& t, uint32_t k) {
   const float sb = e4m3_value(k);
   const float r = __builtin_amdgcn_rcpf(sb * t.st_n);
   const bool fast = t.et >= -80;
-  const float inv = fast ? ldexpf(r, -t.et) : r;
-  const float sts = fast ? t.st : t.st_n;
-  // the two roundings' factors folded into the reciprocal (one product per value
-  // and rounding; y (1 -/+ 2^-20) keeps a margin of about 2^-21 over the few-ulp
-  // error of the approximate quotient)
-  const float invlo = inv * 0.99999905f, invhi = inv * 1.00000095f;
-  float ylo[8], yhi[8];
+  uint32_t clo, chi;
+  if (fast) {
+    const float inv = ldexpf(r, -t.et);
+    // the two roundings' factors folded into the reciprocal (one product per value
+    // and rounding; y (1 -/+ 2^-20) keeps a margin of about 2^-21 over the few-ulp
+    // error of the approximate quotient)
+    const float invlo = inv * 0.99999905f, invhi = inv * 1.00000095f;
+    float ylo[8], yhi[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float xs = fast ? v[i] : ldexpf(v[i], -t.et);
-    ylo[i] = xs * invlo;
-    yhi[i] = xs * invhi;
-  }
-  const uint32_t clo = fp4x8_from_f32(ylo, 1.0f);
-  const uint32_t chi = fp4x8_from_f32(yhi, 1.0f);
-  const uint32_t diff = clo ^ chi;
-  if (diff == 0u) return clo;
-  // Some element lies within 2^-20 of a midpoint: decide exactly the ones that do,
-  // one per iteration (usually one; such elements are rare but can be structural,
-  // e.g. bf16 data whose exact quotients hit midpoints up to the rounding of s_t).
-  uint32_t out = clo;
-  uint32_t pending = diff;
-  while (pending) {
-    const uint32_t sh = (uint32_t)__builtin_ctz(pending) & ~3u;  // bit offset of the nibble
-    pending &= ~(0xFu << sh);
-    const uint32_t lo = (clo >> sh) & 0xFu, hi = (chi >> sh) & 0xFu;
-    float xv = v[0];
+    for (int i = 0; i < 8; ++i) {
+      ylo[i] = v[i] * invlo;
+      yhi[i] = v[i] * invhi;
+    }
+    clo = fp4x8_from_f32(ylo, 1.0f);
+    chi = fp4x8_from_f32(yhi, 1.0f);
+  } else {
+    const float invlo = r * 0.99999905f, invhi = r * 1.00000095f;
+    float ylo[8], yhi[8];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) xv = sh == 4u * j ? v[j] : xv;
-    // the two neighbouring grid values, decoded together: m is their midpoint
-    const f32x2_t g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((lo & 7u) | ((hi & 7u) << 4), 1.0f, 0);
-    const float m = 0.5f * (g.x + g.y);
-    const float xs = fast ? fabsf(xv) : ldexpf(fabsf(xv), -t.et);
-    const float d = fmaf(m * sb, sts, -xs);  // > 0: the quotient is below m
-    const uint32_t c = d > 0.0f ? lo : (d < 0.0f ? hi : ((lo & 1u) ? hi : lo));
-    out = (out & ~(0xFu << sh)) | (c << sh);
+    for (int i = 0; i < 8; ++i) {
+      const float vn = ldexpf(v[i], -t.et);
+      ylo[i] = vn * invlo;
+      yhi[i] = vn * invhi;
+    }
+    clo = fp4x8_from_f32(ylo, 1.0f);
+    chi = fp4x8_from_f32(yhi, 1.0f);
   }
-  return out;
+  if (clo == chi) return clo;
+  return fast ? nv_resolve8(clo, chi, v, 0, sb, t.st) : nv_resolve8(clo, chi, v, -t.et, sb, t.st_n);
+}
+
+// Stochastic rounding of two magnitudes by the carry (e2m1_sr_carry), with the
+// window bits of both folded into `low` by one three-way minimum.
+template <uint32_t K>
+__device__ __forceinline__ void e2m1_sr_carry2(float y0, float y1, uint32_t u0, uint32_t u1, uint32_t& low,
+                                               float& q0, float& q1) {
+  uint32_t l0 = 0xFFFFFFFFu, l1 = 0xFFFFFFFFu;
+  q0 = e2m1_sr_carry<K>(y0, u0, l0);
+  q1 = e2m1_sr_carry<K>(y1, u1, l1);
+  low = min(low, min(l0, l1));
 }
 
 // Codes (sign included) of 8 values of an NVFP4 block with scale code k >= 1,
-// stochastic rounding with words u. With lo and step taken from an approximate
-// quotient, the decision |x| > (lo + step (r + 1/2) 2^-16) s_b s_t is exact (one
-// FMA; the coefficient has at most 23 significant bits). An approximate lo can
-// only be wrong within a few ulp of a grid value, where both candidate decisions
-// return that same grid value, so no correction is needed.
+// stochastic rounding with random values u (r in bits 16..31): the carry decision on
+// the approximate quotient, and where an element lies within its window an exact
+// decision: with lo and step taken from the approximate quotient,
+// |x| > (lo + step (r + 1/2) 2^-16) s_b s_t is exact (one FMA; the coefficient has
+// at most 23 significant bits). An approximate lo can only be wrong within a few
+// ulp of a grid value, where both candidate decisions return that same grid value,
+// so no correction is needed.
 __device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t* u, const NvTensor& t,
                                                  uint32_t k) {
   const float sb = e4m3_value(k);
@@ -509,17 +546,24 @@ __device__ __forceinline__ uint32_t nv_codes8_sr(const float* v, const uint32_t*
   if (t.et >= -80) {
     const float inv = ldexpf(r, -t.et);
     // y carries a relative error below 2^-21 (reciprocal, two products): at most a
-    // few units of F, well inside the window K = 16 of the carry decision
+    // few units of F, well inside the window K = 16 of the carry decision. (The
+    // hardware stochastic conversion would need two conversions per element here, to
+    // bracket the threshold, and costs more than the carry.)
     uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_carry<16>(fabsf(v[i]) * inv, u[i], low), v[i]);
+    for (int i = 0; i < 8; i += 2) {
+      float q0, q1;
+      e2m1_sr_carry2<16>(fabsf(v[i]) * inv, fabsf(v[i + 1]) * inv, u[i], u[i + 1], low, q0, q1);
+      q[i] = with_sign_of(q0, v[i]);
+      q[i + 1] = with_sign_of(q1, v[i + 1]);
+    }
     if (low < 32u) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float ax = fabsf(v[i]);
-        const float y = ax * inv;
+        const float ya = ax * inv;
         float lo, step;
-        e2m1_floor_step(y, lo, step);
+        e2m1_floor_step(ya, lo, step);
         // threshold (lo + step (r + 1/2) 2^-16) s_b, exact (at most 23 significant
         // bits); the sign of c s_t - |x| decides
         const float c = fmaf(step, sr_offset16_plus1(u[i]), lo - step) * sb;

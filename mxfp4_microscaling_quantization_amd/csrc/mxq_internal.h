@@ -29,7 +29,7 @@ struct RowLaunch {
   int64_t rows, cols;
   int dtype;          // 0 bf16, 1 fp32
   int fmt;            // kMX / kNV
-  bool sr;
+  int sr;            // 0 nearest even, 1 stochastic (word stream), 2 stochastic (halves)
   bool rht;
   uint32_t sign_mask;
   uint64_t sr_seed, sr_base;
@@ -48,7 +48,7 @@ struct TileLaunch {
   int64_t rows, cols;
   int dtype;
   int fmt;
-  bool sr;
+  int sr;            // 0 nearest even, 1 stochastic (word stream), 2 stochastic (halves)
   bool rht;
   bool want_row, want_col;
   uint32_t sign_mask;

@@ -43,7 +43,7 @@ __device__ __forceinline__ size_t in_offset(uint32_t c, const RowParams& p) {
   return (size_t)row * (size_t)p.ldx + (size_t)c8 * 8;
 }
 
-template <typename T, int FMT, bool SR, bool RHT, bool CONTIG>
+template <typename T, int FMT, int SR, bool RHT, bool CONTIG>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
   const T* __restrict__ x = reinterpret_cast<const T*>(p.x);
   const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
@@ -63,6 +63,33 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
     if (c < p.chunks) load_raw(x, in_offset<CONTIG>(c, p), raw[j]);
     else zero_raw(raw[j]);
   }
+  // the random values of every chunk first: the generator chains of the chunks are
+  // independent, so they issue interleaved (the encoders below branch per chunk)
+  u32x4 rw[kUnroll][SR == kSrWords ? 2 : 1];
+  if constexpr (SR == kSrWords) {
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint64_t n = p.sr_base + (uint64_t)(base + j * kThreads) * 8;
+      if ((p.sr_base & 3u) == 0u) {  // uniform: whole Philox calls
+        rw[j][0] = philox_words4(n, p.sr_seed);
+        rw[j][1] = philox_words4(n + 4, p.sr_seed);
+      } else {
+        uint32_t u[8];
+        philox_words<8>(n, p.sr_seed, u);
+        rw[j][0] = u32x4{u[0], u[1], u[2], u[3]};
+        rw[j][1] = u32x4{u[4], u[5], u[6], u[7]};
+      }
+    }
+  } else if constexpr (SR == kSrHalves) {
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j)
+      rw[j][0] = philox_halves_words(p.sr_base + (uint64_t)(base + j * kThreads) * 8, p.sr_seed);
+    // keeps the four chains together: left alone, the compiler sinks each into its
+    // chunk's encoder, where it runs as one long dependent chain (measured slower)
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j)
+      asm volatile("" : "+v"(rw[j][0].x), "+v"(rw[j][0].y), "+v"(rw[j][0].z), "+v"(rw[j][0].w));
+  }
 #pragma unroll
   for (int j = 0; j < kUnroll; ++j) {
     const uint32_t c = base + j * kThreads;
@@ -76,9 +103,14 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
       to_f32(raw[j], v);
       if constexpr (RHT) h16_pair(v, threadIdx.x & 1u);
       uint32_t u[8];
-      if constexpr (SR) sr_words8(p.sr_base + (uint64_t)c * 8, p.sr_seed, u);
-      if constexpr (FMT == kMX) packed = mx_encode8<SR, RHT ? 2 : 0>(v, u, byte);
-      else packed = nv_encode8<SR>(v, u, nt, byte);
+      if constexpr (SR == kSrWords) {
+        u[0] = rw[j][0].x; u[1] = rw[j][0].y; u[2] = rw[j][0].z; u[3] = rw[j][0].w;
+        u[4] = rw[j][1].x; u[5] = rw[j][1].y; u[6] = rw[j][1].z; u[7] = rw[j][1].w;
+      } else if constexpr (SR == kSrHalves) {
+        expand_halves(rw[j][0], u);
+      }
+      if constexpr (FMT == kMX) packed = mx_encode8<SR != kRne, RHT ? 2 : 0, sizeof(T) == 2 && !RHT>(v, u, byte);
+      else packed = nv_encode8<SR != kRne>(v, u, nt, byte);
     }
     if (c < p.chunks) {
       reinterpret_cast<uint32_t*>(p.codes)[c] = packed;
@@ -91,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(RowParams p) {
   }
 }
 
-template <typename T, int FMT, bool SR, bool RHT>
+template <typename T, int FMT, int SR, bool RHT>
 static hipError_t launch_rows_t(const RowLaunch& a, hipStream_t st) {
   // slabs of whole rows with fewer than 2^30 chunks keep every index in 32 bits
   const int64_t cpr = a.cols / 8;
@@ -129,8 +161,11 @@ static hipError_t launch_rows_t(const RowLaunch& a, hipStream_t st) {
 
 template <typename T, int FMT>
 static hipError_t launch_rows_f(const RowLaunch& a, hipStream_t st) {
-  if (a.sr) return a.rht ? launch_rows_t<T, FMT, true, true>(a, st) : launch_rows_t<T, FMT, true, false>(a, st);
-  return a.rht ? launch_rows_t<T, FMT, false, true>(a, st) : launch_rows_t<T, FMT, false, false>(a, st);
+  if (a.sr == kSrWords)
+    return a.rht ? launch_rows_t<T, FMT, kSrWords, true>(a, st) : launch_rows_t<T, FMT, kSrWords, false>(a, st);
+  if (a.sr == kSrHalves)
+    return a.rht ? launch_rows_t<T, FMT, kSrHalves, true>(a, st) : launch_rows_t<T, FMT, kSrHalves, false>(a, st);
+  return a.rht ? launch_rows_t<T, FMT, kRne, true>(a, st) : launch_rows_t<T, FMT, kRne, false>(a, st);
 }
 
 hipError_t launch_quantize_rows(const RowLaunch& a, hipStream_t st) {

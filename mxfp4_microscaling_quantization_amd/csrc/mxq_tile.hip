@@ -63,7 +63,7 @@ __device__ __forceinline__ float absmax32(const float* v) {
 
 // MXFP4 encode of 32 values held by one thread (real values times 2^kShift);
 // codes into 4 dwords, returns the block byte.
-template <bool SR, int kShift>
+template <bool SR, int kShift, bool kBf16 = false>
 __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* u, uint32_t out[4]) {
   const uint32_t byte = mx_byte<kShift>(as_u(absmax32(v)));
   const uint32_t b = min(byte, 252u);
@@ -71,11 +71,23 @@ __device__ __forceinline__ uint32_t mx_encode32(const float* v, const uint32_t* 
     const float inv = as_f((254u - b - kShift) << 23);  // exact: a window of K = 1 suffices
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+      if constexpr (kBf16 && kShift == 0) {
+        uint32_t packed;
+        if (mx_sr_hw8(v + 8 * d, u + 8 * d, b, packed)) {
+          out[d] = byte == 255u ? 0u : packed;
+          continue;
+        }
+      }
       float q[8];
       uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        q[i] = with_sign_of(e2m1_sr_carry<1>(fabsf(v[d * 8 + i]) * inv, u[d * 8 + i], low), v[d * 8 + i]);
+      for (int i = 0; i < 8; i += 2) {
+        float q0, q1;
+        e2m1_sr_carry2<1>(fabsf(v[d * 8 + i]) * inv, fabsf(v[d * 8 + i + 1]) * inv, u[d * 8 + i], u[d * 8 + i + 1],
+                          low, q0, q1);
+        q[i] = with_sign_of(q0, v[d * 8 + i]);
+        q[i + 1] = with_sign_of(q1, v[d * 8 + i + 1]);
+      }
       if (low < 2u) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = with_sign_of(e2m1_sr_value(fabsf(v[d * 8 + i]) * inv, u[d * 8 + i]), v[d * 8 + i]);
@@ -128,7 +140,7 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ (((r >> 5) & (G - 1)) * (64 / G));
 }
 
-template <typename T, int FMT, bool SR, bool RHT, bool ROW, bool COL>
+template <typename T, int FMT, int SR, bool RHT, bool ROW, bool COL>
 __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams p) {
   // LDS tile of raw input values, row-major [128][128], XOR-swizzled columns
   using Shape = TileShape<T, FMT, RHT, ROW>;
@@ -206,13 +218,13 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
       to_f32(rr, v);
       if constexpr (RHT) h16_pair(v, t & 1u);
       uint32_t u[8];
-      if constexpr (SR) {
+      if constexpr (SR != kRne) {
         const uint64_t grow = (uint64_t)(p.row0 + r0 + row);
-        sr_words8(p.sr_offset + grow * cols + col, p.sr_seed, u);
+        sr_values<SR, 8>(p.sr_offset + grow * cols + col, p.sr_seed, u);
       }
       uint32_t byte, packed;
-      if constexpr (FMT == kMX) packed = mx_encode8<SR, RHT ? 2 : 0>(v, u, byte);
-      else packed = nv_encode8<SR>(v, u, nt, byte);
+      if constexpr (FMT == kMX) packed = mx_encode8<SR != kRne, RHT ? 2 : 0, sizeof(T) == 2 && !RHT>(v, u, byte);
+      else packed = nv_encode8<SR != kRne>(v, u, nt, byte);
       if (row < nr && col_ok) {
         *reinterpret_cast<uint32_t*>(crow + (uint64_t)(j * kRowStep) * (cols >> 1)) = packed;
         if (col % bs == 0) srow[(uint64_t)(j * kRowStep) * (cols / bs)] = (uint8_t)byte;
@@ -246,18 +258,18 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
       if (vrows > 0 && c < nc) {
         const int64_t grow0 = p.row0 + r0 + h * 32;  // first row of the group in the whole tensor
         uint32_t u[32];
-        if constexpr (SR) philox_words<32>(p.sr_offset + (uint64_t)(col * p.total_rows + grow0), p.sr_seed, u);
+        sr_values<SR, 32>(p.sr_offset + (uint64_t)(col * p.total_rows + grow0), p.sr_seed, u);
         uint8_t* cdst = p.codes_col + col * p.ld_col_codes + grow0 / 2;
         uint8_t* sdst = p.scales_col + col * p.ld_col_scales;
         if constexpr (FMT == kMX) {
           uint32_t out[4];
-          const uint32_t byte = mx_encode32<SR, RHT ? 2 : 0>(v, u, out);
+          const uint32_t byte = mx_encode32<SR != kRne, RHT ? 2 : 0, sizeof(T) == 2 && !RHT>(v, u, out);
           *reinterpret_cast<uint4*>(cdst) = make_uint4(out[0], out[1], out[2], out[3]);
           sdst[grow0 / 32] = (uint8_t)byte;
         } else {
           uint32_t out[4];
-          const uint32_t b0 = nv_encode16<SR>(v, u, nt, out);
-          const uint32_t b1 = nv_encode16<SR>(v + 16, u + 16, nt, out + 2);
+          const uint32_t b0 = nv_encode16<SR != kRne>(v, u, nt, out);
+          const uint32_t b1 = nv_encode16<SR != kRne>(v + 16, u + 16, nt, out + 2);
           // 8-byte stores: rows % 16 == 0 only guarantees 8-byte aligned column runs
           *reinterpret_cast<uint2*>(cdst) = make_uint2(out[0], out[1]);
           sdst[grow0 / 16] = (uint8_t)b0;
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   }
 }
 
-template <typename T, int FMT, bool SR, bool RHT, bool ROW>
+template <typename T, int FMT, int SR, bool RHT, bool ROW>
 static hipError_t launch_tiles_shape(const TileLaunch& a, hipStream_t st) {
   using Shape = TileShape<T, FMT, RHT, ROW>;
   constexpr int kTileR = Shape::R, kTileC = Shape::C, kVGroup = Shape::V;
@@ -314,7 +326,7 @@ static hipError_t launch_tiles_shape(const TileLaunch& a, hipStream_t st) {
   return hipSuccess;
 }
 
-template <typename T, int FMT, bool SR, bool RHT>
+template <typename T, int FMT, int SR, bool RHT>
 static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
   return a.want_row ? launch_tiles_shape<T, FMT, SR, RHT, true>(a, st)
                     : launch_tiles_shape<T, FMT, SR, RHT, false>(a, st);
@@ -322,8 +334,11 @@ static hipError_t launch_tiles_t(const TileLaunch& a, hipStream_t st) {
 
 template <typename T, int FMT>
 static hipError_t launch_tiles_f(const TileLaunch& a, hipStream_t st) {
-  if (a.sr) return a.rht ? launch_tiles_t<T, FMT, true, true>(a, st) : launch_tiles_t<T, FMT, true, false>(a, st);
-  return a.rht ? launch_tiles_t<T, FMT, false, true>(a, st) : launch_tiles_t<T, FMT, false, false>(a, st);
+  if (a.sr == kSrWords)
+    return a.rht ? launch_tiles_t<T, FMT, kSrWords, true>(a, st) : launch_tiles_t<T, FMT, kSrWords, false>(a, st);
+  if (a.sr == kSrHalves)
+    return a.rht ? launch_tiles_t<T, FMT, kSrHalves, true>(a, st) : launch_tiles_t<T, FMT, kSrHalves, false>(a, st);
+  return a.rht ? launch_tiles_t<T, FMT, kRne, true>(a, st) : launch_tiles_t<T, FMT, kRne, false>(a, st);
 }
 
 hipError_t launch_quantize_tiles(const TileLaunch& a, hipStream_t st) {

@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libmxq.so")
 MXQ_OK, MXQ_EINVAL, MXQ_ESHAPE, MXQ_EALIGN, MXQ_EUNSUPPORTED, MXQ_EHIP = range(6)
 BF16, F32 = 0, 1
 MXFP4, NVFP4, NVFP4_2D = 0, 1, 2
-RNE, SR = 0, 1
+RNE, SR, SR16 = 0, 1, 2
 ROWWISE, COLWISE, BOTH = 1, 2, 3
 
 _FMT = {"mxfp4": MXFP4, "nvfp4": NVFP4, "nvfp4_2d": NVFP4_2D}
 _AXIS = {"row": ROWWISE, "col": COLWISE, "both": BOTH}
-_RND = {"rne": RNE, "sr": SR}
+_RND = {"rne": RNE, "sr": SR, "sr16": SR16}
 
 _lib = None
 

@@ -40,3 +40,14 @@ def assert_equal_bits(got: np.ndarray, ref: np.ndarray, what: str):
     if bad.size:
         i = tuple(bad[0])
         raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: got {got[i]!r} expected {ref[i]!r}")
+
+
+def sr_stream(rnd: str, rows: int, cols: int, seed: int, offset: int):
+    """The oracle's random values of a rounding mode for a row-major [rows, cols]
+    tensor: None (nearest even), the word stream ("sr") or the halves stream ("sr16")."""
+    from oracle import philox
+    if rnd == "sr":
+        return philox.tensor_r16(rows, cols, seed, offset)
+    if rnd == "sr16":
+        return philox.tensor_r16_halves(rows, cols, seed, offset)
+    return None

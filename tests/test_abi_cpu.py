@@ -80,6 +80,10 @@ def q(**kw):
     (dict(fmt=2, rows=40), mxq.MXQ_ESHAPE),
     (dict(fmt=2, axis=2, cols=72, ldx=72), mxq.MXQ_ESHAPE),
     (dict(fmt=3), mxq.MXQ_EINVAL),
+    # the halves stream: offsets that are multiples of 8; not for 16x16 NVFP4
+    (dict(rnd=2, off=4), mxq.MXQ_EALIGN),
+    (dict(rnd=2, off=8, cr=FAKE + 4), mxq.MXQ_EALIGN),
+    (dict(fmt=2, rnd=2), mxq.MXQ_EUNSUPPORTED),
 ])
 def test_quantize_validation(kw, status):
     assert q(**kw) == status

@@ -9,14 +9,14 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import f64, require_gpu, u8
+from gpu_helpers import f64, require_gpu, sr_stream, u8
 from mxfp4_microscaling_quantization_amd import mxq
-from oracle import mx, philox, rht
+from oracle import mx, rht
 
 pytestmark = pytest.mark.gpu
 
 R, C = 96, 416
-SEED, OFFSET = 21, 6
+SEED, OFFSET, OFFSET16 = 21, 6, 8
 
 
 def check(codes, scales, y, r16, what):
@@ -29,7 +29,7 @@ def check(codes, scales, y, r16, what):
 
 
 @pytest.mark.parametrize("axis", ["row", "col", "both"])
-@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("rnd", ["rne", "sr", "sr16"])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_rht_mxfp4_variants_exact_inputs(dt, rnd, axis):
     dev = require_gpu()
@@ -38,19 +38,19 @@ def test_rht_mxfp4_variants_exact_inputs(dt, rnd, axis):
     xt = torch.from_numpy(x).to(dt)
     assert np.array_equal(f64(xt), x)  # exact in both input types
     mask = rht.sign_mask_from_seed(13)
-    sr = rnd == "sr"
-    o = mxq.mxq_rht_quantize_mask(xt.to(dev), mask, "mxfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET)
+    off = OFFSET16 if rnd == "sr16" else OFFSET
+    o = mxq.mxq_rht_quantize_mask(xt.to(dev), mask, "mxfp4", axis, rnd, sr_seed=SEED, sr_offset=off)
     what = f"{dt} {rnd} {axis}"
     if axis in ("row", "both"):
-        r16 = philox.tensor_r16(R, C, SEED, OFFSET) if sr else None
+        r16 = sr_stream(rnd, R, C, SEED, off)
         check(u8(o.codes_row), u8(o.scales_row), rht.rht_rowwise(x, mask), r16, what + " row")
     if axis in ("col", "both"):
-        r16t = philox.tensor_r16(C, R, SEED, OFFSET) if sr else None
+        r16t = sr_stream(rnd, C, R, SEED, off)
         check(u8(o.codes_col), u8(o.scales_col), rht.rht_rowwise(x.T.copy(), mask), r16t, what + " col")
 
 
 @pytest.mark.parametrize("axis", ["row", "col"])
-@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("rnd", ["rne", "sr", "sr16"])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_rht_nvfp4_variants_exact_inputs(dt, rnd, axis):
     # the tensor scale belongs to the transformed tensor: its amax (exact here) goes
@@ -64,14 +64,14 @@ def test_rht_nvfp4_variants_exact_inputs(dt, rnd, axis):
     amax = mxq.mxq_rht_amax(xg, mask, axis)
     a_ref = rht.rht_amax(x, mask, axis)
     assert float(amax.item()) == a_ref
-    sr = rnd == "sr"
-    o = mxq.mxq_rht_quantize_mask(xg, mask, "nvfp4", axis, rnd, sr_seed=SEED, sr_offset=OFFSET, amax=amax)
+    off = OFFSET16 if rnd == "sr16" else OFFSET
+    o = mxq.mxq_rht_quantize_mask(xg, mask, "nvfp4", axis, rnd, sr_seed=SEED, sr_offset=off, amax=amax)
     if axis == "row":
-        r16 = philox.tensor_r16(R, C, SEED, OFFSET) if sr else None
+        r16 = sr_stream(rnd, R, C, SEED, off)
         ref_c, ref_s, st = rht.rht_nvfp4_rowwise(x, mask, a_ref, r16)
         y, codes, scales = rht.rht_rowwise(x, mask), u8(o.codes_row), u8(o.scales_row)
     else:
-        r16t = philox.tensor_r16(C, R, SEED, OFFSET) if sr else None
+        r16t = sr_stream(rnd, C, R, SEED, off)
         ref_c, ref_s, st = rht.rht_nvfp4_colwise(x, mask, a_ref, r16t)
         y, codes, scales = rht.rht_rowwise(x.T.copy(), mask), u8(o.codes_col), u8(o.scales_col)
     what = f"nvfp4 {dt} {rnd} {axis}"

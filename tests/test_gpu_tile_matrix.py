@@ -7,18 +7,18 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_equal_bits, bits32, f64, require_gpu, u8
+from gpu_helpers import assert_equal_bits, bits32, f64, require_gpu, sr_stream, u8
 from mxfp4_microscaling_quantization_amd import mxq
-from oracle import mx, nvfp4, philox
+from oracle import mx, nvfp4
 
 pytestmark = pytest.mark.gpu
 
 R, C = 288, 416  # 2 full 128-row tiles + 32 rows; 1 full 256- or 3 full 128-column tiles + the rest
-SEED, OFFSET = 5, 12345  # an offset that is not a multiple of 4
+SEED, OFFSET, OFFSET16 = 5, 12345, 12344  # word stream: an offset that is not a multiple of 4
 
 
 @pytest.mark.parametrize("axis", ["col", "both"])
-@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("rnd", ["rne", "sr", "sr16"])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_tile_kernel_variants(dt, fmt, rnd, axis):
@@ -31,11 +31,11 @@ def test_tile_kernel_variants(dt, fmt, rnd, axis):
     xt = torch.from_numpy(x).to(dt)
     xg = xt.to(dev)
     x64 = f64(xt)
-    sr = rnd == "sr"
-    r16_t = philox.tensor_r16(C, R, SEED, OFFSET) if sr else None
-    r16 = philox.tensor_r16(R, C, SEED, OFFSET) if sr else None
+    off = OFFSET16 if rnd == "sr16" else OFFSET
+    r16_t = sr_stream(rnd, C, R, SEED, off)
+    r16 = sr_stream(rnd, R, C, SEED, off)
     amax = mxq.mxq_amax(xg) if fmt == "nvfp4" else None
-    o = mxq.mxq_quantize(xg, fmt, axis, rnd, sr_seed=SEED, sr_offset=OFFSET, amax=amax)
+    o = mxq.mxq_quantize(xg, fmt, axis, rnd, sr_seed=SEED, sr_offset=off, amax=amax)
     what = f"{dt} {fmt} {rnd} {axis}"
     if fmt == "mxfp4":
         ref_cc, ref_sc = mx.mxfp4_quantize_colwise(x64, r16_t=r16_t)
