@@ -182,6 +182,7 @@ def build_step(wl, dev, sets: int):
 # timing helpers
 
 _busy = None
+_counters_mode = False  # set by --counters: every dispatch is serialised by the profiler
 
 
 def keep_busy(dev, seconds: float = 0.25) -> None:
@@ -192,6 +193,8 @@ def keep_busy(dev, seconds: float = 0.25) -> None:
     import torch
 
     global _busy
+    if _counters_mode:
+        return
     L = stream_lib()
     if _busy is None:
         _busy = torch.empty(2048, dtype=torch.int32, device=dev)
@@ -680,7 +683,14 @@ def main() -> int:
     ap.add_argument("--no-next", action="store_true", help="skip the rows beyond the step and the ablation")
     ap.add_argument("--no-refs", action="store_true", help="skip the streaming references and the VALU probe")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph timing of configuration 1")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc passes: no clock-holding busy loops, no graph timing, and of the "
+                         "references only the 1 GiB copy (which scales FETCH_SIZE / WRITE_SIZE) and the VALU probe")
     args = ap.parse_args()
+    if args.counters:
+        global _counters_mode
+        _counters_mode = True
+        args.no_graph = True
     if args.gpus != 1:
         print("bench.py measures one MI355X: the quantisation kernels need no collectives and this "
               "build runs on a single GPU; --gpus must be 1", file=sys.stderr)
@@ -750,7 +760,7 @@ def main() -> int:
     refs, valu_ref = None, None
     if not args.no_refs:
         refs = {}
-        for k in kernels:
+        for k in ([] if args.counters else kernels):
             key = f"{k.cfg}.{k.name}"
             if k.mix[0] == "tile":
                 R, C = (int(v) for v in k.shape.split("x"))
