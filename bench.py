@@ -35,9 +35,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 CUS, SIMDS_PER_CU, CLOCK_HZ = 256, 4, 2.4e9
-# A wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles: the chip issues
-# at most CUS * SIMDS_PER_CU * CLOCK_HZ / 4 wave instructions per second.
-VALU_WAVE_INST_PEAK = CUS * SIMDS_PER_CU * CLOCK_HZ / 4
+# The published fp32 vector peak, 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 32 lanes x 2
+# flops x 2.4 GHz, means a SIMD retires a wave64 VALU instruction every 2 cycles: the
+# chip issues at most CUS * SIMDS_PER_CU * CLOCK_HZ / 2 wave instructions per second.
+VALU_WAVE_INST_PEAK = CUS * SIMDS_PER_CU * CLOCK_HZ / 2
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 VALU_FILE = os.path.join(PROFILES, "valu.json")
@@ -800,6 +801,8 @@ def main() -> int:
         valu[key] = {"valu_wave_insts_per_launch": winst,
                      "valu_insts_per_element": round(winst * 64 / elements[key], 3),
                      "wave_inst_per_s": round(rate / 1e9, 1), "frac_of_issue_peak": round(rate / VALU_WAVE_INST_PEAK, 4)}
+        if valu_ref:  # against what independent v_add_u32 chains reach on this chip
+            valu[key]["frac_of_probe_rate"] = round(rate / (valu_ref["v_add_u32"]["wave_inst_per_s"] * 1e9), 4)
     if valu_ref:
         valu["probe"] = valu_ref
 
