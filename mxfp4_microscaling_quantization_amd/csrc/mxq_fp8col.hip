@@ -174,29 +174,42 @@ __device__ __forceinline__ void exact_convert(const RcParams& p, int64_t t0, int
   }
 }
 
-// Writes bytes [lo, hi) of a 16-byte output piece (0 <= lo < hi <= 16) with as few
-// aligned stores as the range allows.
+// Writes bytes [lo, hi) of a 16-byte output piece (0 <= lo < hi <= 16, not the whole
+// piece, which the callers store as one 16-byte store) as at most
+// seven naturally aligned stores, each under its own predicate (no loop: the lanes
+// of a wave that store partial pieces start and end at different bytes, and a
+// per-lane loop would issue the union of all their paths). From b = lo upwards: a
+// byte to reach 2-byte alignment, a short to reach 4, a dword to reach 8, an 8-byte
+// store when 8 aligned bytes remain, then a dword, a short and a byte for the rest.
 __device__ __forceinline__ void store_partial(uint8_t* g, const uint32_t* o, int lo, int hi) {
-  if (lo == 0 && hi >= 8) {  // the piece that ends an expert's run
-    *reinterpret_cast<uint2*>(g) = make_uint2(o[0], o[1]);
-    lo = 8;
-  } else if (hi == 16 && lo <= 8) {  // the piece that starts a run
-    *reinterpret_cast<uint2*>(g + 8) = make_uint2(o[2], o[3]);
-    hi = 8;
+  // the dword holding byte b (b < 16), by selects rather than a dynamic index
+  auto dword = [&](int b) { const int i = b >> 2; return i == 0 ? o[0] : i == 1 ? o[1] : i == 2 ? o[2] : o[3]; };
+  int b = lo;
+  if ((b & 1) && b < hi) {
+    g[b] = (uint8_t)(dword(b) >> (8 * (b & 3)));
+    b += 1;
   }
-  for (int b = lo; b < hi;) {
-    const uint32_t word = o[b >> 2];
-    if ((b & 3) == 0 && b + 4 <= hi) {
-      *reinterpret_cast<uint32_t*>(g + b) = word;
-      b += 4;
-    } else if ((b & 1) == 0 && b + 2 <= hi) {
-      *reinterpret_cast<uint16_t*>(g + b) = (uint16_t)(word >> (8 * (b & 3)));
-      b += 2;
-    } else {
-      g[b] = (uint8_t)(word >> (8 * (b & 3)));
-      b += 1;
-    }
+  if ((b & 2) && b + 2 <= hi) {
+    *reinterpret_cast<uint16_t*>(g + b) = (uint16_t)(dword(b) >> (8 * (b & 3)));
+    b += 2;
   }
+  if ((b & 4) && b + 4 <= hi) {
+    *reinterpret_cast<uint32_t*>(g + b) = dword(b);
+    b += 4;
+  }
+  if ((b & 7) == 0 && b + 8 <= hi) {
+    *reinterpret_cast<uint2*>(g + b) = b == 0 ? make_uint2(o[0], o[1]) : make_uint2(o[2], o[3]);
+    b += 8;
+  }
+  if (b + 4 <= hi) {
+    *reinterpret_cast<uint32_t*>(g + b) = dword(b);
+    b += 4;
+  }
+  if (b + 2 <= hi) {
+    *reinterpret_cast<uint16_t*>(g + b) = (uint16_t)(dword(b) >> (8 * (b & 3)));
+    b += 2;
+  }
+  if (b < hi) g[b] = (uint8_t)(dword(b) >> (8 * (b & 3)));
 }
 
 __global__ __launch_bounds__(kRcThreads, 3) void fp4_row_to_fp8_col_kernel(RcParams p) {
