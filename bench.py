@@ -563,6 +563,15 @@ def extra_rows(wl, dev, reps: int, traffic: dict) -> tuple[dict, dict]:
         lambda k: mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off, out=outs[k]), n,
         Nb // 2 + Nb // 32 + Nb + 4 * Cb * G + 8 * len(w.offsets), Nb,
         f"MXFP4 tokens of 256 experts (the cfg3 split) -> E4M3 of the transpose, {G} groups of 128 tokens")
+    # the same buffer split into 256 experts of 256 tokens: every group starts on a
+    # 128-byte output line (how much of the time the ragged split's unaligned group
+    # runs cost)
+    off_al = torch.arange(0, Rb + 1, Rb // 256, dtype=torch.int64, device=dev)
+    G_al = Rb // 128
+    row("fp4_row_to_fp8_col_aligned_experts", "cfg3", f"{Rb}x{Cb}",
+        lambda k: mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off_al, out=outs[k]), n,
+        Nb // 2 + Nb // 32 + Nb + 4 * Cb * G_al + 8 * 257, Nb,
+        "the same buffer as 256 experts of 256 tokens (every group line-aligned): the cost of unaligned experts")
     del codes, e8, outs
     torch.cuda.empty_cache()
     return rows, abl
