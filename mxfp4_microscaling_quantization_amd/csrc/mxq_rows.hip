@@ -20,6 +20,10 @@ namespace mxq {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr uint32_t kChunksPerWG = kThreads * kUnroll;
+// Dequantisation writes 4x what it reads; with 2 chunks per lane its stores stream
+// measurably faster than with 4 (more workgroups in flight, each shorter).
+constexpr int kDeqUnroll = 2;
+constexpr uint32_t kDeqChunksPerWG = kThreads * kDeqUnroll;
 
 struct RowParams {
   const void* x;
@@ -217,7 +221,7 @@ __device__ __forceinline__ uint32_t bf16_of_product(float a, float st_scaled, in
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
-  const uint32_t base = blockIdx.x * kChunksPerWG + threadIdx.x;
+  const uint32_t base = blockIdx.x * kDeqChunksPerWG + threadIdx.x;
   float st = 0.0f, st_s = 0.0f;
   int k = 0;
   if constexpr (FMT == kNV) {
@@ -225,10 +229,10 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
     k = (fabsf(st) < 0x1p-60f) ? 64 : 0;
     st_s = ldexpf(st, k);
   }
-  uint32_t w[kUnroll];
-  uint32_t sb[kUnroll];
+  uint32_t w[kDeqUnroll];
+  uint32_t sb[kDeqUnroll];
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
+  for (int j = 0; j < kDeqUnroll; ++j) {
     const uint32_t c = base + j * kThreads;
     w[j] = 0;
     sb[j] = 0;
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
+  for (int j = 0; j < kDeqUnroll; ++j) {
     const uint32_t c = base + j * kThreads;
     if (c >= p.chunks) continue;
     uint4 ov;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DeqParams p) {
 // lines (a lane owning 8 elements would write its 32 bytes as two half-lines).
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void dequant_f32_kernel(DeqParams p) {
-  constexpr int kU = 2 * kUnroll;
+  constexpr int kU = 2 * kDeqUnroll;
   const uint32_t units = p.chunks * 2u;
   const uint32_t base = blockIdx.x * (kThreads * kU) + threadIdx.x;
   const uint16_t* codes = reinterpret_cast<const uint16_t*>(p.codes);
@@ -362,8 +366,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int fm
     p.chunks = (uint32_t)(nr * cpr);
     p.tensor_scale = tensor_scale;
     p.y = reinterpret_cast<uint8_t*>(y) + (size_t)r0 * cols * osz;
-    const uint32_t grid = (p.chunks + kChunksPerWG - 1) / kChunksPerWG;
-    // both kernels cover kChunksPerWG chunks (8 elements each) per workgroup
+    const uint32_t grid = (p.chunks + kDeqChunksPerWG - 1) / kDeqChunksPerWG;
+    // both kernels cover kDeqChunksPerWG chunks (8 elements each) per workgroup
     if (fmt == kMX) {
       if (out_dtype == 0) hipLaunchKernelGGL((dequant_kernel<kMX>), dim3(grid), dim3(kThreads), 0, st, p);
       else hipLaunchKernelGGL((dequant_f32_kernel<kMX>), dim3(grid), dim3(kThreads), 0, st, p);
