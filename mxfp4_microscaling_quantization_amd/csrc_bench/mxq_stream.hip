@@ -40,14 +40,14 @@ struct Vec<16> {
 // read only). Lane t of workgroup b takes units b * 1024 + j * 256 + t, so every
 // load and store instruction of a wave covers one contiguous run, as in the codec
 // kernels. NTL / NTS: nontemporal loads / stores.
-template <int RB, int WB, bool NTL, bool NTS>
+template <int RB, int WB, bool NTL, bool NTS, int U>
 __global__ __launch_bounds__(kThreads) void stream_mix_kernel(const uint8_t* __restrict__ src,
                                                               uint8_t* __restrict__ dst, uint32_t units) {
   typedef typename Vec<RB>::T RT;
-  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-  RT v[kUnroll];
+  const uint32_t base = blockIdx.x * (kThreads * U) + threadIdx.x;
+  RT v[U];
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
+  for (int j = 0; j < U; ++j) {
     const uint32_t u = base + j * kThreads;
     const RT* p = reinterpret_cast<const RT*>(src) + u;
     if (u < units) v[j] = NTL ? __builtin_nontemporal_load(p) : *p;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void stream_mix_kernel(const uint8_t* __r
   }
   uint32_t acc = 0;
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
+  for (int j = 0; j < U; ++j) {
     const uint32_t u = base + j * kThreads;
     const uint32_t f = Vec<RB>::fold(v[j]);
     if constexpr (WB > 0) {
@@ -75,17 +75,26 @@ __global__ __launch_bounds__(kThreads) void stream_mix_kernel(const uint8_t* __r
   }
 }
 
-template <int RB, int WB>
-hipError_t launch_mix(const void* src, void* dst, int64_t units, int flags, hipStream_t st) {
-  const uint32_t grid = (uint32_t)((units + kThreads * kUnroll - 1) / (kThreads * kUnroll));
+template <int RB, int WB, int U>
+hipError_t launch_mix_u(const void* src, void* dst, int64_t units, int flags, hipStream_t st) {
+  const uint32_t grid = (uint32_t)((units + kThreads * U - 1) / (kThreads * U));
   const bool ntl = flags & 1, nts = flags & 2;
   const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
   uint8_t* d = reinterpret_cast<uint8_t*>(dst);
-  if (ntl && nts) hipLaunchKernelGGL((stream_mix_kernel<RB, WB, true, true>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
-  else if (ntl) hipLaunchKernelGGL((stream_mix_kernel<RB, WB, true, false>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
-  else if (nts) hipLaunchKernelGGL((stream_mix_kernel<RB, WB, false, true>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
-  else hipLaunchKernelGGL((stream_mix_kernel<RB, WB, false, false>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
+  if (ntl && nts) hipLaunchKernelGGL((stream_mix_kernel<RB, WB, true, true, U>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
+  else if (ntl) hipLaunchKernelGGL((stream_mix_kernel<RB, WB, true, false, U>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
+  else if (nts) hipLaunchKernelGGL((stream_mix_kernel<RB, WB, false, true, U>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
+  else hipLaunchKernelGGL((stream_mix_kernel<RB, WB, false, false, U>), dim3(grid), dim3(kThreads), 0, st, s, d, (uint32_t)units);
   return hipGetLastError();
+}
+
+// flags bits 2-3: lane units per thread, 0 -> kUnroll, 1 -> 1, 2 -> 2
+template <int RB, int WB>
+hipError_t launch_mix(const void* src, void* dst, int64_t units, int flags, hipStream_t st) {
+  const int u = (flags >> 2) & 3;
+  if (u == 1) return launch_mix_u<RB, WB, 1>(src, dst, units, flags, st);
+  if (u == 2) return launch_mix_u<RB, WB, 2>(src, dst, units, flags, st);
+  return launch_mix_u<RB, WB, kUnroll>(src, dst, units, flags, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,13 +205,13 @@ int mxq_valu_probe(void* out, int blocks, int iters, int kind, void* stream) {
 
 // Streaming mix: `units` units of rd_bytes read and wr_bytes written (rd in {4, 8,
 // 16}, wr in {0, 4, 8, 16}); flags bit 0 nontemporal loads, bit 1 nontemporal
-// stores. src holds units * rd bytes, dst units * wr bytes (read only: one dword per
+// stores, bits 2-3 lane units per thread (0: 4, 1: 1, 2: 2; 3 is rejected). src holds units * rd bytes, dst units * wr bytes (read only: one dword per
 // 1024 units). 0 < units < 2^31. Returns 0, 1 for an unsupported mix or size, 2 for a
 // launch failure.
 int mxq_stream_mix(const void* src, void* dst, int64_t units, int rd_bytes, int wr_bytes, int flags,
                    void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (units <= 0 || units >= ((int64_t)1 << 31)) return 1;
+  if (units <= 0 || units >= ((int64_t)1 << 31) || ((flags >> 2) & 3) == 3) return 1;
   hipError_t e;
   if (rd_bytes == 16 && wr_bytes == 4) e = launch_mix<16, 4>(src, dst, units, flags, st);
   else if (rd_bytes == 4 && wr_bytes == 16) e = launch_mix<4, 16>(src, dst, units, flags, st);
