@@ -1,5 +1,10 @@
 // Column-wise (and fused row + column) quantisation from one read of the input.
 //
+// Two kernels. bf16 input with nearest-even rounding (MXFP4 both ways, NVFP4
+// column-wise) walks 256-column strips (quantize_strip_kernel below): the column
+// codes of 256 rows leave as whole 128-byte lines. Everything else (fp32 input,
+// stochastic rounding, NVFP4 with both outputs) uses the tile kernel:
+//
 // A 256-thread workgroup owns one tile (shape per variant, see TileShape; 32 KB of
 // LDS, 64 KB for the fused MXFP4 tile). Phase 1: every thread loads 16-byte chunks
 // (a wave reads whole 256- or 512-byte row segments per instruction), quantises
@@ -14,6 +19,7 @@
 // one XCD in consecutive turns, so the pieces of a 128-byte line of column codes
 // are written through the same L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "mxq_blocks.h"
 #include "mxq_internal.h"
@@ -283,8 +289,313 @@ __global__ __launch_bounds__(kTileThreads) void quantize_tile_kernel(TileParams 
   }
 }
 
+// ---- Strip walker (bf16 input).
+//
+// A workgroup owns a strip of 256 columns and walks down it in 64-row steps, one
+// flush unit of 256 rows after another. Each step: the raw tile goes to LDS (with
+// the column transform's signs), the row-wise blocks are quantised from registers as
+// in the tile kernel, and the column tasks (one column over 32 rows, two per thread)
+// encode from LDS into registers. After four steps a column holds 256 rows of codes,
+// one 128-byte line: the lines are assembled in LDS and leave as whole-line stores,
+// and the column scales leave as one run per column. Row scales are staged in LDS
+// and leave as one run per row. The next step's input is loaded while the current
+// step's column tasks run.
+constexpr int kStripC = 256;  // columns of a strip
+constexpr int kStepR = 64;    // rows of a step
+constexpr int kFlushR = 256;  // rows of a flush unit
+
+struct StripParams {
+  const uint16_t* x;
+  int64_t ldx;
+  int64_t rows, cols;     // slab extent
+  int64_t total_rows;     // whole tensor (column-wise SR index and strides)
+  int64_t row0;           // slab's first row in the whole tensor (a multiple of kFlushR)
+  uint32_t strips;        // strips across the slab
+  uint32_t flushes;       // flush units down the slab
+  uint32_t per_wg;        // flush units per workgroup
+  uint32_t units;         // workgroups down one strip
+  uint32_t sign_mask;
+  uint64_t sr_seed, sr_offset;
+  uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
+  int64_t ld_col_codes, ld_col_scales;
+  const float* amax;
+  int st_given;
+  float* tensor_scale;
+};
+
+// Stores bytes [0, n) of an LDS run (16-byte aligned, n <= 16) at p: dword stores
+// when p and n allow them, else byte stores.
+__device__ __forceinline__ void store_run(uint8_t* p, const uint8_t* src, int n) {
+  if ((((uintptr_t)p | (uintptr_t)n) & 3u) == 0) {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+    uint32_t* d = reinterpret_cast<uint32_t*>(p);
+    if ((((uintptr_t)p) & 7u) == 0 && n >= 8) {
+      *reinterpret_cast<uint2*>(d) = make_uint2(s[0], s[1]);
+      if (n == 12) d[2] = s[2];
+      if (n == 16) *reinterpret_cast<uint2*>(d + 2) = make_uint2(s[2], s[3]);
+    } else {
+      for (int i = 0; i < (n >> 2); ++i) d[i] = s[i];
+    }
+  } else {
+    for (int i = 0; i < n; ++i) p[i] = src[i];
+  }
+}
+
+// The lane index as a value the compiler cannot see through: per-lane addresses
+// derived from it are recomputed where they are used instead of being held in
+// registers across the whole walk.
+__device__ __forceinline__ uint32_t opaque_lane() {
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+template <int FMT, int SR, bool RHT, bool ROW>
+__global__ __launch_bounds__(kTileThreads) void quantize_strip_kernel(StripParams p) {
+  constexpr int bs = FMT == kMX ? 32 : 16;
+  constexpr int kChunksPerRow = kStripC / 8;                // 32 lanes per row
+  constexpr int kRowStep = kTileThreads / kChunksPerRow;    // 8 rows between a thread's chunks
+  constexpr int kChunks = kStepR / kRowStep;                // 8 chunks per thread and step
+  static_assert(kRowStep == 8 && kChunks == 8, "chunk layout");
+  // bf16 tile of a step (XOR-swizzled as in the tile kernel), then the column-code
+  // lines of a flush unit (column c at c * 128, 16-byte slot s at (s ^ (c & 7)) * 16)
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kStepR * kStripC * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t rsc[kStepR * 16];   // row scales of a step
+  __shared__ __attribute__((aligned(16))) uint8_t csc[kStripC * 16];  // column scales of a flush unit
+  NvTensor nt;
+  if constexpr (FMT == kNV) {
+    nt = nv_tensor_load(p.amax, p.st_given);
+    if (p.tensor_scale && blockIdx.x == 0 && threadIdx.x == 0) *p.tensor_scale = nt.st;
+    if constexpr (RHT) nv_tensor_times4(nt);
+  }
+
+  const uint32_t unit = blockIdx.x / p.strips, strip = blockIdx.x - unit * p.strips;
+  if (unit >= p.units) return;
+  const uint32_t f0 = unit * p.per_wg, f1 = min(f0 + p.per_wg, p.flushes);
+  const int64_t c0 = (int64_t)strip * kStripC;
+  const int nc = (int)std::min<int64_t>(kStripC, p.cols - c0);
+  const uint64_t ldx = (uint64_t)p.ldx;
+  const uint64_t cols = (uint64_t)p.cols;
+
+  // A thread's chunks: column cc * 8 of the strip, rows row_t + 8 j of the step.
+  Raw<uint16_t> cur[kChunks];
+  auto load_chunk = [&](int64_t r0, int j, uint32_t t) {
+    const int cc = (int)(t % kChunksPerRow), row_t = (int)(t / kChunksPerRow);
+    const int nr = (int)std::min<int64_t>(kStepR, p.rows - r0);
+    const uint16_t* xs = p.x + (uint64_t)(r0 + row_t) * ldx + (uint64_t)c0 + (uint64_t)(cc * 8);
+    if (row_t + j * kRowStep < nr && cc * 8 < nc) load_raw(xs, (uint64_t)(j * kRowStep) * ldx, cur[j]);
+    else zero_raw(cur[j]);
+  };
+  auto load_step = [&](int64_t r0) {
+    const uint32_t t = opaque_lane();
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) load_chunk(r0, j, t);
+  };
+  load_step((int64_t)f0 * kFlushR);
+
+#pragma unroll 1
+  for (uint32_t f = f0; f < f1; ++f) {
+    const int64_t fr = (int64_t)f * kFlushR;
+    const int vrows = (int)std::min<int64_t>(kFlushR, p.rows - fr);  // valid rows of the unit
+    uint32_t acc[4][2][4] = {};  // steps past the last row stay zero
+    uint32_t scol[2][2] = {{0u, 0u}, {0u, 0u}};  // column scale bytes of the unit's steps
+    // the four steps of the unit, written out (a compile-time step index keeps the
+    // code registers statically addressed)
+    auto step = [&](auto sq_c) {
+      constexpr int sq = decltype(sq_c)::value;
+      const int64_t r0 = fr + sq * kStepR;
+      if (r0 < p.rows) {
+        const int nr = (int)std::min<int64_t>(kStepR, p.rows - r0);
+        __syncthreads();  // the previous step's (or flush's) LDS reads are done
+        // ---- phase 1: park the raw tile, quantise rows from registers
+        {
+          const uint32_t t = opaque_lane();
+          const int cc = (int)(t % kChunksPerRow), row_t = (int)(t / kChunksPerRow);
+          const bool col_ok = cc * 8 < nc;
+          const uint64_t col = (uint64_t)c0 + (uint64_t)(cc * 8);
+          // rows row_t + 8 j lie in the first 32-row group for j < 4 and in the
+          // second for j >= 4 (swizzled column cc * 8 ^ 32)
+          uint8_t* const wr0 = buf + (row_t * kStripC + cc * 8) * 2;
+          uint8_t* const wr1 = buf + (row_t * kStripC + ((cc * 8) ^ 32)) * 2;
+          uint8_t* const crow = ROW ? p.codes_row + (uint64_t)(r0 + row_t) * (cols >> 1) + (col >> 1) : nullptr;
+#pragma unroll
+          for (int j = 0; j < kChunks; ++j) {
+            const int row = row_t + j * kRowStep;
+            uint8_t* const w = (j < 4 ? wr0 : wr1) + j * kRowStep * kStripC * 2;
+            if constexpr (RHT) {
+              // the column transform's sign of this row (its position mod 16)
+              Raw<uint16_t> sr = cur[j];
+              flip_all(sr, (p.sign_mask >> ((row_t + 8 * (j & 1)) & 15)) & 1u);
+              *reinterpret_cast<Raw<uint16_t>*>(w) = sr;
+            } else {
+              *reinterpret_cast<Raw<uint16_t>*>(w) = cur[j];
+            }
+            if constexpr (ROW) {
+              Raw<uint16_t> rr = cur[j];
+              if constexpr (RHT) flip(rr, make_flips<uint16_t>(p.sign_mask, t & 1u));
+              float v[8];
+              to_f32(rr, v);
+              if constexpr (RHT) h16_pair(v, t & 1u);
+              uint32_t u[8];
+              if constexpr (SR != kRne) {
+                const uint64_t grow = (uint64_t)(p.row0 + r0 + row);
+                sr_values<SR, 8>(p.sr_offset + grow * cols + col, p.sr_seed, u);
+              }
+              uint32_t byte, packed;
+              if constexpr (FMT == kMX) packed = mx_encode8<SR != kRne, RHT ? 2 : 0, !RHT>(v, u, byte);
+              else packed = nv_encode8<SR != kRne>(v, u, nt, byte);
+              if (row < nr && col_ok) {
+                *reinterpret_cast<uint32_t*>(crow + (uint64_t)(j * kRowStep) * (cols >> 1)) = packed;
+                if ((cc * 8) % bs == 0) rsc[row * 16 + (cc * 8) / bs] = (uint8_t)byte;
+              }
+            }
+          }
+        }
+        // next step's input, in flight while the column tasks run
+        asm volatile("" ::: "memory");
+        if (r0 + kStepR < p.rows && (sq < 3 || f + 1 < f1)) load_step(r0 + kStepR);
+        __syncthreads();
+        const uint32_t t = opaque_lane();
+        if constexpr (ROW) {
+          if ((int)t < nr)
+            store_run(p.scales_row + (uint64_t)(r0 + t) * (cols / bs) + (uint64_t)c0 / bs, rsc + t * 16, nc / bs);
+        }
+        // ---- phase 2: column tasks (column k / 2, 32-row group k % 2 for k = t + 256 m),
+        // codes to registers. Group h reads rows 32 h .. 32 h + 31, whose swizzled
+        // column is c ^ 32 h; column c + 128 sits 256 bytes further.
+        const int h = (int)(t & 1u);
+        const uint8_t* const rd = buf + (h * 32 * kStripC + (((int)(t >> 1)) ^ (32 * h))) * 2;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int c = (int)(t >> 1) + 128 * m;
+          float v[32];
+#pragma unroll
+          for (int i = 0; i < 32; ++i)
+            v[i] = as_f((uint32_t)(*reinterpret_cast<const uint16_t*>(rd + 256 * m + i * kStripC * 2)) << 16);
+          if constexpr (RHT) {
+            h16_local(v);
+            h16_local(v + 16);
+          }
+          uint32_t u[32];
+          if constexpr (SR != kRne) {
+            const uint64_t grow0 = (uint64_t)(p.row0 + r0 + h * 32);
+            sr_values<SR, 32>(p.sr_offset + (uint64_t)(c0 + c) * (uint64_t)p.total_rows + grow0, p.sr_seed, u);
+          }
+          if constexpr (FMT == kMX) {
+            const uint32_t byte = mx_encode32<SR != kRne, RHT ? 2 : 0, !RHT>(v, u, acc[sq][m]);
+            scol[m][0] |= byte << (8 * sq);
+          } else {
+            const uint32_t b0 = nv_encode16<SR != kRne>(v, u, nt, acc[sq][m]);
+            const uint32_t b1 = nv_encode16<SR != kRne>(v + 16, u + 16, nt, acc[sq][m] + 2);
+            scol[m][sq >> 1] |= (b0 | (b1 << 8)) << (16 * (sq & 1));
+          }
+          // keep one task's values from being held across the next task's reads
+          asm volatile("" ::"v"(acc[sq][m][0]), "v"(acc[sq][m][1]), "v"(acc[sq][m][2]), "v"(acc[sq][m][3]) : "memory");
+        }
+      }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    // ---- flush: whole 128-byte lines of column codes, one scale run per column.
+    // Task (c, h) has c = t / 2 + 128 m, so c & 7 does not depend on m: the line
+    // slot of step q is (2 q + h) ^ (c & 7).
+    __syncthreads();
+    {
+      const uint32_t t = opaque_lane();
+      const int ch = (int)(t >> 1), h = (int)(t & 1u), sw = ch & 7;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int c = ch + 128 * m;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<uint4*>(buf + c * 128 + (((2 * q + h) ^ sw) * 16)) =
+              make_uint4(acc[q][m][0], acc[q][m][1], acc[q][m][2], acc[q][m][3]);
+          if constexpr (FMT == kMX) csc[c * 16 + 2 * q + h] = (uint8_t)(scol[m][0] >> (8 * q));
+          else *reinterpret_cast<uint16_t*>(csc + c * 16 + 4 * q + 2 * h) = (uint16_t)(scol[m][q >> 1] >> (16 * (q & 1)));
+        }
+      }
+    }
+    __syncthreads();
+    {
+      // piece j = t % 8 of column t / 8 + 32 it: one LDS base and one global base
+      const uint32_t t = opaque_lane();
+      const int c8 = (int)(t >> 3), j = (int)(t & 7u);
+      const int left = vrows - 32 * j;  // valid rows of the piece's 32-row group
+      const uint8_t* lsrc = buf + c8 * 128 + ((j ^ (c8 & 7)) * 16);
+      uint8_t* dst = p.codes_col + (uint64_t)(c0 + c8) * (uint64_t)p.ld_col_codes + (uint64_t)(p.row0 + fr) / 2 + 16 * j;
+      const uint64_t dstep = 32 * (uint64_t)p.ld_col_codes;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        if (c8 + 32 * it < nc && left > 0) {
+          const uint4 w = *reinterpret_cast<const uint4*>(lsrc + it * 32 * 128);
+          uint8_t* d = dst + it * dstep;
+          if (FMT == kMX || (left >= 32 && ((uintptr_t)d & 15u) == 0)) {
+            *reinterpret_cast<uint4*>(d) = w;
+          } else {
+            // NVFP4 column runs are only 8-byte aligned; a group may hold 16 valid rows
+            *reinterpret_cast<uint2*>(d) = make_uint2(w.x, w.y);
+            if (left >= 32) *reinterpret_cast<uint2*>(d + 8) = make_uint2(w.z, w.w);
+          }
+        }
+      }
+      if ((int)t < nc)
+        store_run(p.scales_col + (uint64_t)(c0 + t) * (uint64_t)p.ld_col_scales + (uint64_t)(p.row0 + fr) / bs,
+                  csc + t * 16, vrows / bs);
+    }
+  }
+}
+
+template <int FMT, int SR, bool RHT, bool ROW>
+static hipError_t launch_strips(const TileLaunch& a, hipStream_t st) {
+  const int64_t strips = (a.cols + kStripC - 1) / kStripC;
+  // slabs of at most 2^22 workgroups, on flush-unit boundaries
+  const int64_t max_rows = (int64_t)kFlushR * std::max<int64_t>(1, ((int64_t)1 << 22) / strips);
+  for (int64_t s0 = 0; s0 < a.rows; s0 += max_rows) {
+    const int64_t nr = std::min(max_rows, a.rows - s0);
+    StripParams p;
+    p.x = reinterpret_cast<const uint16_t*>(a.x) + (size_t)s0 * a.ldx;
+    p.ldx = a.ldx;
+    p.rows = nr;
+    p.cols = a.cols;
+    p.total_rows = a.total_rows;
+    p.row0 = a.row0 + s0;
+    p.strips = (uint32_t)strips;
+    const int64_t flushes = (nr + kFlushR - 1) / kFlushR;
+    p.flushes = (uint32_t)flushes;
+    // about four resident workgroups per CU on 256 CUs; longer walks once that is met
+    p.per_wg = (uint32_t)std::min<int64_t>(4, std::max<int64_t>(1, flushes * strips / 1024));
+    p.units = (uint32_t)((flushes + p.per_wg - 1) / p.per_wg);
+    p.sign_mask = a.sign_mask;
+    p.sr_seed = a.sr_seed;
+    p.sr_offset = a.sr_offset;
+    const int bs = FMT == kMX ? 32 : 16;
+    p.codes_row = a.codes_row ? a.codes_row + s0 * (a.cols / 2) : nullptr;
+    p.scales_row = a.scales_row ? a.scales_row + s0 * (a.cols / bs) : nullptr;
+    p.codes_col = a.codes_col;
+    p.scales_col = a.scales_col;
+    p.ld_col_codes = a.ld_col_codes;
+    p.ld_col_scales = a.ld_col_scales;
+    p.amax = a.amax;
+    p.st_given = a.st_given ? 1 : 0;
+    p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
+    const uint32_t grid = p.units * p.strips;
+    hipLaunchKernelGGL((quantize_strip_kernel<FMT, SR, RHT, ROW>), dim3(grid), dim3(kTileThreads), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename T, int FMT, int SR, bool RHT, bool ROW>
 static hipError_t launch_tiles_shape(const TileLaunch& a, hipStream_t st) {
+  // bf16 with nearest-even rounding walks strips (NVFP4 column-wise only); stochastic
+  // rounding's random words and the NVFP4 row side need more registers than the
+  // walk leaves for four resident workgroups per CU, and stay on tiles.
+  if constexpr (sizeof(T) == 2 && SR == kRne && !(FMT == kNV && ROW)) {
+    if (a.row0 % kFlushR == 0) return launch_strips<FMT, SR, RHT, ROW>(a, st);
+  }
   using Shape = TileShape<T, FMT, RHT, ROW>;
   constexpr int kTileR = Shape::R, kTileC = Shape::C, kVGroup = Shape::V;
   // slabs of at most 2^22 tiles (cols <= 2^30 gives at most 2^23 tiles per tile row)
