@@ -162,7 +162,7 @@ def build_step(wl, dev, sets: int):
                fp8_bytes(n3), n3, (8, 16, 3), n3 // 2),
         Kernel("rht_mxfp4_rowcol", "cfg4", sh4,
                lambda k: mxq.mxq_rht_quantize(S[k]["x4"], seed4, "mxfp4", "both", out=S[k]["rq"]),
-               2 * n4 + 2 * (n4 // 2 + n4 // 32), n4, ("tile", 64), 2 * n4),
+               2 * n4 + 2 * (n4 // 2 + n4 // 32), n4, ("strip",), 2 * n4),
         Kernel("nvfp4_amax", "cfg5", sh5,
                lambda k: mxq.mxq_amax(S[k]["x5a"], out=S[k]["amax"]), 2 * n5 + 4, n5, (16, 0, 1), 2 * n5),
         Kernel("nvfp4_quantize_rne", "cfg5", sh5,
@@ -262,9 +262,9 @@ def stream_lib():
         L = ctypes.CDLL(p)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L.mxq_stream_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
-        L.mxq_stream_tile_pattern.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp]
+        L.mxq_stream_strip_pattern.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.mxq_valu_probe.argtypes = [vp, i32, i32, i32, vp]
-        for n in ("mxq_stream_mix", "mxq_stream_tile_pattern", "mxq_valu_probe"):
+        for n in ("mxq_stream_mix", "mxq_stream_strip_pattern", "mxq_valu_probe"):
             getattr(L, n).restype = i32
         _stream_lib = L
     return _stream_lib
@@ -311,8 +311,9 @@ def _stream_mix_once(dev, read_bytes: int, rd: int, wr: int, flags: int, reps: i
     return out
 
 
-def tile_pattern_reference(dev, rows: int, cols: int, tile_rows: int, reps: int, sets: int = 3) -> dict:
-    """The fused row + column tile kernel's exact access pattern, moving bytes only."""
+def strip_pattern_reference(dev, rows: int, cols: int, reps: int, sets: int = 3) -> dict:
+    """The fused row + column strip kernel's access pattern (bf16 MXFP4 row + column),
+    moving bytes only."""
     import torch
 
     L = stream_lib()
@@ -323,10 +324,10 @@ def tile_pattern_reference(dev, rows: int, cols: int, tile_rows: int, reps: int,
 
     def fn(k):
         o = outs[k]
-        rc = L.mxq_stream_tile_pattern(xs[k].data_ptr(), rows, cols, tile_rows, o[0].data_ptr(), o[1].data_ptr(),
-                                       o[2].data_ptr(), o[3].data_ptr(), st)
+        rc = L.mxq_stream_strip_pattern(xs[k].data_ptr(), rows, cols, o[0].data_ptr(), o[1].data_ptr(),
+                                        o[2].data_ptr(), o[3].data_ptr(), st)
         if rc:
-            raise RuntimeError(f"mxq_stream_tile_pattern returned {rc}")
+            raise RuntimeError(f"mxq_stream_strip_pattern returned {rc}")
 
     for k in range(sets):
         fn(k)
@@ -335,7 +336,7 @@ def tile_pattern_reference(dev, rows: int, cols: int, tile_rows: int, reps: int,
     n = rows * cols
     out = figures(us, 2 * n + 2 * (n // 2 + n // 32), n)
     out.pop("elements_per_s")
-    out.update({"tile": f"{tile_rows}x256", "shape": f"{rows}x{cols}"})
+    out.update({"strip": "256 columns x 256-row units", "shape": f"{rows}x{cols}"})
     del xs, outs
     torch.cuda.empty_cache()
     return out
@@ -783,10 +784,10 @@ def main() -> int:
         refs = {}
         for k in ([] if args.counters else kernels):
             key = f"{k.cfg}.{k.name}"
-            if k.mix[0] == "tile":
+            if k.mix[0] == "strip":
                 R, C = (int(v) for v in k.shape.split("x"))
-                ref = tile_pattern_reference(dev, R, C, k.mix[1], args.kernel_reps)
-                ref["pattern"] = f"fused row + column tile pattern, {k.mix[1]}x256 tiles"
+                ref = strip_pattern_reference(dev, R, C, args.kernel_reps)
+                ref["pattern"] = "fused row + column strip pattern: 256-column strips, whole 128-byte column-code lines"
             else:
                 rd, wr, fl = k.mix
                 ref = stream_mix_reference(dev, k.read_bytes, rd, wr, fl, args.kernel_reps)

@@ -5,6 +5,8 @@
 // nothing, so their throughput on the same sizes is what that memory traffic can
 // reach on this chip.
 #include <hip/hip_runtime.h>
+#include <type_traits>
+#include <algorithm>
 #include <stdint.h>
 
 namespace {
@@ -98,58 +100,110 @@ hipError_t launch_mix(const void* src, void* dst, int64_t units, int flags, hipS
 }
 
 // ---------------------------------------------------------------------------
-// The fused row + column tile pattern: a bf16 [R, C] tensor read in TR x TC tiles
-// (TC = 256), each 16-byte chunk folded to 4 bytes at the row-code position and one
-// byte per 32-element row block at the row-scale position; the tile parked in LDS;
-// then, per column and 32-row group, 16 bytes at the column-code position [C, R/2]
-// and one byte at the column-scale position [C, R/32]. Workgroups are dealt to the
-// XCDs as the tile kernel deals them (V vertically adjacent tiles per XCD turn).
-template <int TR>
-__global__ __launch_bounds__(kThreads) void tile_pattern_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                                int64_t cols, uint8_t* codes_row, uint8_t* scales_row,
-                                                                uint8_t* codes_col, uint8_t* scales_col,
-                                                                uint32_t tiles_r, uint32_t tiles_c, uint32_t groups) {
-  constexpr int TC = 256, G = TR / 32, V = 256 / TR;
-  constexpr int kChunksPerRow = TC / 8, kRowStep = kThreads / kChunksPerRow, kChunks = TR * TC / 8 / kThreads;
-  __shared__ uint16_t tile[TR][TC] __attribute__((aligned(16)));
-  const uint32_t t = threadIdx.x;
-  const uint32_t xcd = blockIdx.x & 7u, slot = blockIdx.x >> 3;
-  const uint32_t g = (slot / V) * 8u + xcd;
-  if (g >= groups) return;
-  const uint32_t gr = g / tiles_c, tc = g - gr * tiles_c;
-  const uint32_t tr = gr * V + slot % V;
-  if (tr >= tiles_r) return;
-  const int64_t r0 = (int64_t)tr * TR, c0 = (int64_t)tc * TC;
-  const int cc = (int)(t % kChunksPerRow), row_t = (int)(t / kChunksPerRow);
-  const uint16_t* xt = x + (r0 + row_t) * cols + c0 + cc * 8;
-  u32x4 cur[kChunks];
+// The fused row + column strip pattern (the bf16 MXFP4 row + column kernel's memory
+// traffic, moving bytes only): a workgroup walks a 256-column strip in 64-row steps
+// over `per_wg` units of 256 rows. Each step parks the tile in LDS, folds each
+// 16-byte chunk to 4 bytes at the row-code position, stages one byte per 32-element
+// row block and stores it as one 8-byte run per row; the column tasks (one column
+// over 32 rows) fold 32 values to 16 bytes kept in registers. After four steps the
+// column codes leave as whole 128-byte lines assembled in LDS and the column scales
+// as one 8-byte run per column.
+__device__ __forceinline__ uint32_t opaque_lane() {
+  uint32_t t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__global__ __launch_bounds__(kThreads) void strip_pattern_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                                 int64_t cols, uint8_t* codes_row, uint8_t* scales_row,
+                                                                 uint8_t* codes_col, uint8_t* scales_col,
+                                                                 uint32_t strips, uint32_t flushes, uint32_t per_wg) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[64 * 256 * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t rsc[64 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t csc[256 * 8];
+  const uint32_t unit = blockIdx.x / strips, strip = blockIdx.x - unit * strips;
+  const uint32_t f0 = unit * per_wg, f1 = min(f0 + per_wg, flushes);
+  if (f0 >= flushes) return;
+  const int64_t c0 = (int64_t)strip * 256;
+  u32x4 cur[8];
+  auto load_step = [&](int64_t r0) {
+    const uint32_t t = opaque_lane();
+    const uint16_t* xs = x + (r0 + (t >> 5)) * cols + c0 + (t & 31u) * 8;
 #pragma unroll
-  for (int j = 0; j < kChunks; ++j)
-    cur[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xt + (int64_t)(j * kRowStep) * cols));
-  uint8_t* crow = codes_row + (r0 + row_t) * (cols / 2) + (c0 + cc * 8) / 2;
-  uint8_t* srow = scales_row + (r0 + row_t) * (cols / 32) + (c0 + cc * 8) / 32;
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    const int row = row_t + j * kRowStep;
-    const int sc = (cc * 8) ^ (((row >> 5) & (G - 1)) * (64 / G));
-    *reinterpret_cast<u32x4*>(&tile[row][sc]) = cur[j];
-    const uint32_t f = cur[j].x ^ cur[j].y ^ cur[j].z ^ cur[j].w;
-    *reinterpret_cast<uint32_t*>(crow + (int64_t)(j * kRowStep) * (cols / 2)) = f;
-    if ((cc & 3) == 0) srow[(int64_t)(j * kRowStep) * (cols / 32)] = (uint8_t)f;
-  }
-  __syncthreads();
+    for (int j = 0; j < 8; ++j) cur[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + (int64_t)(8 * j) * cols));
+  };
+  load_step((int64_t)f0 * 256);
 #pragma unroll 1
-  for (int k = t; k < TC * G; k += kThreads) {
-    const int c = k / G, h = k % G;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (uint32_t f = f0; f < f1; ++f) {
+    const int64_t fr = (int64_t)f * 256;
+    uint32_t acc[4][2][4];
+    uint32_t scol[2] = {0u, 0u};
+    auto step = [&](auto sq_c) {
+      constexpr int sq = decltype(sq_c)::value;
+      const int64_t r0 = fr + sq * 64;
+      __syncthreads();
+      {
+        const uint32_t t = opaque_lane();
+        const int cc = (int)(t & 31u), row_t = (int)(t >> 5);
+        uint8_t* const wr0 = buf + (row_t * 256 + cc * 8) * 2;
+        uint8_t* const wr1 = buf + (row_t * 256 + ((cc * 8) ^ 32)) * 2;
+        uint8_t* const crow = codes_row + (r0 + row_t) * (cols / 2) + (c0 + cc * 8) / 2;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int r = h * 32 + i;
-      w[i >> 3] ^= (uint32_t)tile[r][c ^ (((r >> 5) & (G - 1)) * (64 / G))] << (4 * (i & 7));
+        for (int j = 0; j < 8; ++j) {
+          *reinterpret_cast<u32x4*>((j < 4 ? wr0 : wr1) + j * 8 * 256 * 2) = cur[j];
+          const uint32_t v = cur[j].x ^ cur[j].y ^ cur[j].z ^ cur[j].w;
+          *reinterpret_cast<uint32_t*>(crow + (int64_t)(8 * j) * (cols / 2)) = v;
+          if ((cc & 3) == 0) rsc[(row_t + 8 * j) * 8 + cc / 4] = (uint8_t)v;
+        }
+      }
+      asm volatile("" ::: "memory");
+      if (sq < 3 || f + 1 < f1) load_step(r0 + 64);
+      __syncthreads();
+      const uint32_t t = opaque_lane();
+      if (t < 64) *reinterpret_cast<uint2*>(scales_row + (r0 + t) * (cols / 32) + c0 / 32) = *reinterpret_cast<const uint2*>(rsc + t * 8);
+      const int h = (int)(t & 1u);
+      const uint8_t* const rd = buf + (h * 32 * 256 + (((int)(t >> 1)) ^ (32 * h))) * 2;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          w[i >> 3] ^= (uint32_t)(*reinterpret_cast<const uint16_t*>(rd + 256 * m + i * 512)) << (4 * (i & 7));
+        asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]) : "memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[sq][m][q] = w[q];
+        scol[m] |= ((w[0] ^ w[3]) & 0xFFu) << (8 * sq);
+      }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    __syncthreads();
+    {
+      const uint32_t t = opaque_lane();
+      const int ch = (int)(t >> 1), h = (int)(t & 1u), sw = ch & 7;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int c = ch + 128 * m;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<u32x4*>(buf + c * 128 + (((2 * q + h) ^ sw) * 16)) = u32x4{acc[q][m][0], acc[q][m][1], acc[q][m][2], acc[q][m][3]};
+          csc[c * 8 + 2 * q + h] = (uint8_t)(scol[m] >> (8 * q));
+        }
+      }
     }
-    const int64_t col = c0 + c, grow0 = r0 + h * 32;
-    *reinterpret_cast<u32x4*>(codes_col + col * (rows / 2) + grow0 / 2) = u32x4{w[0], w[1], w[2], w[3]};
-    scales_col[col * (rows / 32) + grow0 / 32] = (uint8_t)(w[0] ^ w[3]);
+    __syncthreads();
+    {
+      const uint32_t t = opaque_lane();
+      const int c8 = (int)(t >> 3), j = (int)(t & 7u);
+      const uint8_t* lsrc = buf + c8 * 128 + ((j ^ (c8 & 7)) * 16);
+      uint8_t* dst = codes_col + (c0 + c8) * (rows / 2) + fr / 2 + 16 * j;
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+        *reinterpret_cast<u32x4*>(dst + (int64_t)it * 32 * (rows / 2)) = *reinterpret_cast<const u32x4*>(lsrc + it * 4096);
+      *reinterpret_cast<uint2*>(scales_col + (c0 + t) * (rows / 32) + fr / 32) = *reinterpret_cast<const uint2*>(csc + t * 8);
+    }
   }
 }
 
@@ -223,26 +277,21 @@ int mxq_stream_mix(const void* src, void* dst, int64_t units, int rd_bytes, int 
   return e == hipSuccess ? 0 : 2;
 }
 
-// The fused row + column tile access pattern over a bf16 [rows, cols] tensor
-// (rows % tile_rows == 0, cols % 256 == 0, tile_rows 64 or 128); outputs sized as
-// the MXFP4 row- and column-wise outputs. Returns 0, 1 for bad sizes, 2 for a
-// launch failure.
-int mxq_stream_tile_pattern(const void* x, int64_t rows, int64_t cols, int tile_rows, void* codes_row,
-                            void* scales_row, void* codes_col, void* scales_col, void* stream) {
+// The fused row + column strip access pattern over a bf16 [rows, cols] tensor
+// (rows % 256 == 0, cols % 256 == 0), with as many 256-row units per workgroup as
+// the bf16 MXFP4 row + column kernel takes; outputs sized as the MXFP4 row- and
+// column-wise outputs. Returns 0, 1 for bad sizes, 2 for a launch failure.
+int mxq_stream_strip_pattern(const void* x, int64_t rows, int64_t cols, void* codes_row, void* scales_row,
+                             void* codes_col, void* scales_col, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (rows <= 0 || cols <= 0 || cols % 256 || (tile_rows != 64 && tile_rows != 128) || rows % tile_rows) return 1;
-  const uint32_t tiles_r = (uint32_t)(rows / tile_rows), tiles_c = (uint32_t)(cols / 256);
-  const uint32_t V = 256 / tile_rows;
-  const uint32_t groups = ((tiles_r + V - 1) / V) * tiles_c;
-  const uint32_t grid = 8u * V * ((groups + 7u) / 8u);
-  const uint16_t* xs = reinterpret_cast<const uint16_t*>(x);
-  uint8_t *a = (uint8_t*)codes_row, *b = (uint8_t*)scales_row, *c = (uint8_t*)codes_col, *d = (uint8_t*)scales_col;
-  if (tile_rows == 64)
-    hipLaunchKernelGGL((tile_pattern_kernel<64>), dim3(grid), dim3(kThreads), 0, st, xs, rows, cols, a, b, c, d,
-                       tiles_r, tiles_c, groups);
-  else
-    hipLaunchKernelGGL((tile_pattern_kernel<128>), dim3(grid), dim3(kThreads), 0, st, xs, rows, cols, a, b, c, d,
-                       tiles_r, tiles_c, groups);
+  if (rows <= 0 || cols <= 0 || cols % 256 || rows % 256 || rows >= ((int64_t)1 << 30)) return 1;
+  const int64_t strips = cols / 256, flushes = rows / 256;
+  const int64_t per_wg = std::min<int64_t>(4, std::max<int64_t>(1, flushes * strips / 1024));
+  const int64_t units = (flushes + per_wg - 1) / per_wg;
+  if (units * strips >= ((int64_t)1 << 31)) return 1;
+  hipLaunchKernelGGL(strip_pattern_kernel, dim3((uint32_t)(units * strips)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const uint16_t*>(x), rows, cols, (uint8_t*)codes_row, (uint8_t*)scales_row,
+                     (uint8_t*)codes_col, (uint8_t*)scales_col, (uint32_t)strips, (uint32_t)flushes, (uint32_t)per_wg);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
