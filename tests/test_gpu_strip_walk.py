@@ -108,3 +108,60 @@ def test_strip_walk_sampled_against_oracle():
     ref_c, ref_s = mx.mxfp4_quantize_rowwise(x64.T.copy())
     assert_equal_bits(u8(o.codes_col[torch.from_numpy(cs).to(xb.device)]), ref_c, "sampled column codes")
     assert_equal_bits(u8(o.scales_col[torch.from_numpy(cs).to(xb.device)]), ref_s, "sampled column scales")
+
+
+SMALL = [(32, 8), (32, 264), (64, 256), (96, 544), (288, 40), (288, 288)]
+
+
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_strip_walk_small_and_strided_against_oracle(shape, fmt, rht):
+    """Tiny and strided bf16 inputs through the strip kernel (one partial strip, fewer
+    than 64 rows, a last strip of 8 columns), against the oracle: bit-exact without
+    the transform; with it, against the fp32 path (the transform's fp32 sums are
+    the same on both paths). The strided input is a column window of a wider
+    tensor (row stride 48 elements more than the width, 16-byte aligned)."""
+    from gpu_helpers import assert_equal_bits, f64, u8
+    from oracle import mx, nvfp4
+
+    dev = require_gpu()
+    R, C = shape
+    axis = "both" if C % (32 if fmt == "mxfp4" else 16) == 0 and not (fmt == "nvfp4" and rht) else "col"
+    rng = np.random.default_rng(R * 31 + C)
+    x = rng.standard_normal((R, C)) * np.exp2(rng.integers(-9, 9, (R, 1)) + rng.integers(-3, 3, (1, C)))
+    x[rng.random((R, C)) < 0.03] = 0.0
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    wide = torch.zeros((R, C + 48), dtype=torch.bfloat16)
+    wide[:, 16:16 + C] = xt
+    xs = wide.to(dev)[:, 16:16 + C]  # strided view
+    xc = xt.to(dev)
+    amax = mxq.mxq_amax(xc) if fmt == "nvfp4" else None
+    o_s = _run(xs, fmt, axis, "rne", rht, amax)
+    o_c = _run(xc, fmt, axis, "rne", rht, amax)
+    what = f"{R}x{C} {fmt} {axis} rht={rht}"
+    for name in ("codes_col", "scales_col", "codes_row", "scales_row"):
+        a, b = getattr(o_s, name), getattr(o_c, name)
+        if a is not None:
+            assert torch.equal(a, b), f"{what} {name}: strided differs from contiguous"
+    if rht:
+        o_f = _run(xc.float(), fmt, axis, "rne", rht, amax)
+        for name in ("codes_col", "scales_col", "codes_row", "scales_row"):
+            a, b = getattr(o_c, name), getattr(o_f, name)
+            if a is not None:
+                assert torch.equal(a, b), f"{what} {name}: bf16 differs from fp32"
+        return
+    x64 = f64(xt)
+    if fmt == "mxfp4":
+        ref_cc, ref_sc = mx.mxfp4_quantize_colwise(x64)
+    else:
+        ref_cc, ref_sc, _ = nvfp4.nvfp4_quantize_colwise(x64)
+    assert_equal_bits(u8(o_c.codes_col), ref_cc, what + " column codes")
+    assert_equal_bits(u8(o_c.scales_col), ref_sc, what + " column scales")
+    if axis == "both":
+        if fmt == "mxfp4":
+            ref_cr, ref_sr = mx.mxfp4_quantize_rowwise(x64)
+        else:
+            ref_cr, ref_sr, _ = nvfp4.nvfp4_quantize_rowwise(x64)
+        assert_equal_bits(u8(o_c.codes_row), ref_cr, what + " row codes")
+        assert_equal_bits(u8(o_c.scales_row), ref_sr, what + " row scales")
