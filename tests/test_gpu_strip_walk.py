@@ -165,3 +165,43 @@ def test_strip_walk_small_and_strided_against_oracle(shape, fmt, rht):
             ref_cr, ref_sr, _ = nvfp4.nvfp4_quantize_rowwise(x64)
         assert_equal_bits(u8(o_c.codes_row), ref_cr, what + " row codes")
         assert_equal_bits(u8(o_c.scales_row), ref_sr, what + " row scales")
+
+
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("case", ["zeros", "nan", "inf", "huge", "one_big_block", "tiny_fp32"])
+def test_nvfp4_colwise_special_tensors(case, rnd):
+    """NVFP4 column-wise on special tensors (s_t zero, NaN, huge, one block holding the
+    amax, an fp32-subnormal s_t), against the oracle; bf16 with nearest-even rounding
+    runs the strip kernel, the other cases the tile kernel."""
+    from gpu_helpers import assert_equal_bits, bits32, f64, u8
+    from oracle import nvfp4, philox
+
+    dev = require_gpu()
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((48, 320))
+    dt = torch.bfloat16
+    if case == "zeros":
+        x[:] = 0.0
+        x[3, 7] = -0.0
+    elif case == "nan":
+        x[5, 5] = np.nan
+    elif case == "inf":
+        x[17, 300] = -np.inf
+    elif case == "huge":
+        x = x * 1e37
+    elif case == "one_big_block":
+        x[20, 260] = 1e30  # every other block's scale underflows E4M3
+    elif case == "tiny_fp32":
+        x = x * 1e-40
+        dt = torch.float32
+    xt = torch.from_numpy(x).to(dt)
+    xg = xt.to(dev)
+    x64 = f64(xt)
+    amax = mxq.mxq_amax(xg)
+    o = mxq.mxq_quantize(xg, "nvfp4", "col", rnd, sr_seed=7, sr_offset=0, amax=amax)
+    r16t = philox.tensor_r16(x64.shape[1], x64.shape[0], seed=7, offset=0) if rnd == "sr" else None
+    ref_c, ref_s, st = nvfp4.nvfp4_quantize_colwise(x64, r16_t=r16t)
+    ts = bits32(o.tensor_scale)[0]
+    assert ts == np.float32(st).view(np.uint32) or (np.isnan(st) and ts == 0x7FC00000), (case, hex(ts), st)
+    assert_equal_bits(u8(o.scales_col), ref_s, f"{case} {rnd} column scales")
+    assert_equal_bits(u8(o.codes_col), ref_c, f"{case} {rnd} column codes")
