@@ -350,8 +350,10 @@ __device__ __forceinline__ uint32_t opaque_lane() {
   return t;
 }
 
+// Four workgroups per CU (what the 37 KB of LDS allows): the register bound this asks
+// for (128) fits every variant without spills.
 template <int FMT, int SR, bool RHT, bool ROW>
-__global__ __launch_bounds__(kTileThreads) void quantize_strip_kernel(StripParams p) {
+__global__ __launch_bounds__(kTileThreads, 4) void quantize_strip_kernel(StripParams p) {
   constexpr int bs = FMT == kMX ? 32 : 16;
   constexpr int kChunksPerRow = kStripC / 8;                // 32 lanes per row
   constexpr int kRowStep = kTileThreads / kChunksPerRow;    // 8 rows between a thread's chunks
