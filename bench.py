@@ -263,8 +263,9 @@ def stream_lib():
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L.mxq_stream_mix.argtypes = [vp, vp, i64, i32, i32, i32, vp]
         L.mxq_stream_strip_pattern.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+        L.mxq_stream_2d_pattern.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.mxq_valu_probe.argtypes = [vp, i32, i32, i32, vp]
-        for n in ("mxq_stream_mix", "mxq_stream_strip_pattern", "mxq_valu_probe"):
+        for n in ("mxq_stream_mix", "mxq_stream_strip_pattern", "mxq_stream_2d_pattern", "mxq_valu_probe"):
             getattr(L, n).restype = i32
         _stream_lib = L
     return _stream_lib
@@ -311,32 +312,33 @@ def _stream_mix_once(dev, read_bytes: int, rd: int, wr: int, flags: int, reps: i
     return out
 
 
-def strip_pattern_reference(dev, rows: int, cols: int, reps: int, sets: int = 3) -> dict:
-    """The fused row + column strip kernel's access pattern (bf16 MXFP4 row + column),
-    moving bytes only."""
+def pattern_reference(dev, kind: str, rows: int, cols: int, reps: int, sets: int = 3) -> dict:
+    """A fused row + column kernel's access pattern, moving bytes only: kind "strip" (the
+    bf16 MXFP4 row + column strip kernel) or "2d" (16x16 NVFP4, W and W^T)."""
     import torch
 
     L = stream_lib()
+    bs = 32 if kind == "strip" else 16
     e = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
     xs = [torch.full((rows, cols), k + 1, dtype=torch.bfloat16, device=dev) for k in range(sets)]
-    outs = [(e(rows, cols // 2), e(rows, cols // 32), e(cols, rows // 2), e(cols, rows // 32)) for _ in range(sets)]
+    outs = [(e(rows, cols // 2), e(rows, cols // bs), e(cols, rows // 2), e(cols, rows // bs)) for _ in range(sets)]
     st = torch.cuda.current_stream().cuda_stream
+    call = L.mxq_stream_strip_pattern if kind == "strip" else L.mxq_stream_2d_pattern
 
     def fn(k):
         o = outs[k]
-        rc = L.mxq_stream_strip_pattern(xs[k].data_ptr(), rows, cols, o[0].data_ptr(), o[1].data_ptr(),
-                                        o[2].data_ptr(), o[3].data_ptr(), st)
+        rc = call(xs[k].data_ptr(), rows, cols, o[0].data_ptr(), o[1].data_ptr(), o[2].data_ptr(), o[3].data_ptr(), st)
         if rc:
-            raise RuntimeError(f"mxq_stream_strip_pattern returned {rc}")
+            raise RuntimeError(f"{kind} pattern reference returned {rc}")
 
     for k in range(sets):
         fn(k)
     keep_busy(dev)
     us = avg_launch_us(fn, sets, reps)
     n = rows * cols
-    out = figures(us, 2 * n + 2 * (n // 2 + n // 32), n)
+    out = figures(us, 2 * n + 2 * (n // 2 + n // bs), n)
     out.pop("elements_per_s")
-    out.update({"strip": "256 columns x 256-row units", "shape": f"{rows}x{cols}"})
+    out.update({"pattern_kind": kind, "shape": f"{rows}x{cols}"})
     del xs, outs
     torch.cuda.empty_cache()
     return out
@@ -424,7 +426,7 @@ def config1_report(wl, dev, reps: int, graph: bool = True) -> list:
     return out
 
 
-def extra_rows(wl, dev, reps: int, traffic: dict) -> tuple[dict, dict]:
+def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[dict, dict]:
     """The rows beyond the step, each at its own workload with rotating input copies:
     NVFP4 amax + quantise as one call (the amax computed by the call), 16x16-scaled
     NVFP4 of a 14336 x 4096 FFN weight (both outputs), RHT + NVFP4 column-wise and
@@ -481,6 +483,13 @@ def extra_rows(wl, dev, reps: int, traffic: dict) -> tuple[dict, dict]:
         2 * Nw + 2 * (Nw // 2 + Nw // 16) + 4, Nw, "14336x4096 FFN weight (outlier law, seed 5), 16x16 block "
         "scales, W and W^T codes from one read")
     del ws, am, q2
+    if refs:  # what the kernel's access pattern reaches when it moves bytes only
+        ref = pattern_reference(dev, "2d", Rw, Cw, reps)
+        rows["nvfp4_2d_rowcol"]["stream_ref_GB_s"] = ref["GB_s"]
+        rows["nvfp4_2d_rowcol"]["frac_of_stream_ref"] = round(rows["nvfp4_2d_rowcol"]["GB_s"] / ref["GB_s"], 4)
+        rows["nvfp4_2d_rowcol"]["stream_ref_pattern"] = "16x16 NVFP4 tile pattern, bytes only"
+        print(f"[ref]   nvfp4_2d_rowcol {ref['GB_s']:8.1f} GB/s (16x16 NVFP4 tile pattern); kernel at "
+              f"{100 * rows['nvfp4_2d_rowcol']['frac_of_stream_ref']:.1f}%", file=sys.stderr, flush=True)
     # gradient recipes on the cfg4 tensor
     x4 = [wl["cfg4"].x.to(dev) for _ in range(n)]
     R4, C4 = x4[0].shape
@@ -786,7 +795,7 @@ def main() -> int:
             key = f"{k.cfg}.{k.name}"
             if k.mix[0] == "strip":
                 R, C = (int(v) for v in k.shape.split("x"))
-                ref = strip_pattern_reference(dev, R, C, args.kernel_reps)
+                ref = pattern_reference(dev, "strip", R, C, args.kernel_reps)
                 ref["pattern"] = "fused row + column strip pattern: 256-column strips, whole 128-byte column-code lines"
             else:
                 rd, wr, fl = k.mix
@@ -836,7 +845,7 @@ def main() -> int:
     if not args.no_next:
         del kernels
         torch.cuda.empty_cache()
-        nxt, abl = extra_rows(wl, dev, args.kernel_reps, traffic)
+        nxt, abl = extra_rows(wl, dev, args.kernel_reps, traffic, refs=not (args.no_refs or args.counters))
 
     line = {
         "metric": "quantize/convert GB/s (in+out bytes) and % of MI355X HBM peak, per kernel",

@@ -1,9 +1,9 @@
 // Streaming reference kernels for the benchmark (libmxq_stream.so, not part of the
 // quantisation library): plain copies with the read/write byte mix of each codec
-// kernel, and a byte mover with the tile kernels' exact access pattern. They move
-// the same bytes in the same order as the kernels they stand beside and compute
-// nothing, so their throughput on the same sizes is what that memory traffic can
-// reach on this chip.
+// kernel, and byte movers with the access patterns of the fused row + column kernel
+// and of the 16x16 NVFP4 kernel. They move the same bytes in the same order as the
+// kernels they stand beside and compute nothing, so their throughput on the same
+// sizes is what that memory traffic can reach on this chip.
 #include <hip/hip_runtime.h>
 #include <type_traits>
 #include <algorithm>
@@ -208,6 +208,68 @@ __global__ __launch_bounds__(kThreads) void strip_pattern_kernel(const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
+// The 16x16 NVFP4 pattern (the bf16 W and W^T kernel's memory traffic, moving bytes
+// only): a workgroup owns a 128 x 128 tile; the four lanes of a quad own a 16 x 16
+// block, each an 8 x 8 quarter (8 rows of one 16-byte chunk), folded to 4 bytes per
+// row at the row-code position; the quarter's eight column dwords go through LDS and
+// leave as 16-byte pieces, four lanes (64 bytes) per column; one 8-byte run per row
+// and per column of the tile for the scales. The 16 tiles of a 4 x 4 superblock go to
+// one XCD in consecutive turns, as in the kernel.
+__global__ __launch_bounds__(kThreads) void pattern_2d_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                              uint8_t* codes_row, uint8_t* scales_row,
+                                                              uint8_t* codes_col, uint8_t* scales_col, uint32_t tiles_c,
+                                                              uint32_t sb_c, uint32_t sbs) {
+  __shared__ uint32_t ct[128][16];
+  __shared__ uint32_t kblk[64];
+  const uint32_t t = threadIdx.x;
+  const uint32_t xcd = blockIdx.x & 7u, slot = blockIdx.x >> 3;
+  const uint32_t sb = (slot >> 4) * 8u + xcd, w = slot & 15u;
+  if (sb >= sbs) return;
+  const uint32_t sbr = sb / sb_c, sbc = sb - sbr * sb_c;
+  const uint32_t tr = 4u * sbr + (w >> 2), tc = 4u * sbc + (w & 3u);
+  if ((int64_t)tr * 128 >= rows || tc >= tiles_c) return;
+  const int64_t r0 = (int64_t)tr * 128, c0 = (int64_t)tc * 128;
+  const int b = (int)(t >> 2), q = (int)(t & 3u);
+  const int row0 = (b >> 3) * 16 + (q >> 1) * 8, col0 = (b & 7) * 16 + (q & 1) * 8;
+  const uint16_t* xq = x + (r0 + row0) * cols + c0 + col0;
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xq + (int64_t)i * cols));
+  uint32_t code[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) code[i] = v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  uint8_t* crow = codes_row + (r0 + row0) * (cols / 2) + (c0 + col0) / 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(crow + (int64_t)i * (cols / 2)) = code[i];
+  if (q == 0) kblk[b] = code[0] & 0xFFu;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ct[col0 + j][row0 >> 3] = code[j] ^ (uint32_t)j;
+  __syncthreads();
+  if (t < 128) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= kblk[(t >> 4) * 8 + i] << (8 * i);
+      hi |= kblk[(t >> 4) * 8 + 4 + i] << (8 * i);
+    }
+    *reinterpret_cast<u32x2*>(scales_row + (r0 + t) * (cols / 16) + c0 / 16) = u32x2{lo, hi};
+    uint32_t clo = 0, chi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      clo |= kblk[i * 8 + (t >> 4)] << (8 * i);
+      chi |= kblk[(4 + i) * 8 + (t >> 4)] << (8 * i);
+    }
+    *reinterpret_cast<u32x2*>(scales_col + (c0 + t) * (rows / 16) + r0 / 16) = u32x2{clo, chi};
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int pc = (int)t + k * 256, c = pc >> 2, h = pc & 3;
+    __builtin_nontemporal_store(u32x4{ct[c][4 * h], ct[c][4 * h + 1], ct[c][4 * h + 2], ct[c][4 * h + 3]},
+                                reinterpret_cast<u32x4*>(codes_col + (c0 + c) * (rows / 2) + (r0 + h * 32) / 2));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // VALU issue probe: every lane runs `iters` iterations of eight independent
 // dependency chains of one instruction kind (written out, so each iteration issues
 // exactly eight VALU instructions): 0 v_add_u32, 1 v_bitop3_b32, 2 v_mad_u64_u32.
@@ -292,6 +354,22 @@ int mxq_stream_strip_pattern(const void* x, int64_t rows, int64_t cols, void* co
   hipLaunchKernelGGL(strip_pattern_kernel, dim3((uint32_t)(units * strips)), dim3(kThreads), 0, st,
                      reinterpret_cast<const uint16_t*>(x), rows, cols, (uint8_t*)codes_row, (uint8_t*)scales_row,
                      (uint8_t*)codes_col, (uint8_t*)scales_col, (uint32_t)strips, (uint32_t)flushes, (uint32_t)per_wg);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The 16x16 NVFP4 access pattern over a bf16 [rows, cols] tensor (both multiples of
+// 128); outputs sized as the NVFP4 row- and column-wise outputs. Returns 0, 1 for bad
+// sizes, 2 for a launch failure.
+int mxq_stream_2d_pattern(const void* x, int64_t rows, int64_t cols, void* codes_row, void* scales_row,
+                          void* codes_col, void* scales_col, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (rows <= 0 || cols <= 0 || rows % 128 || cols % 128 || rows / 128 * (cols / 128) >= ((int64_t)1 << 24)) return 1;
+  const uint32_t tiles_r = (uint32_t)(rows / 128), tiles_c = (uint32_t)(cols / 128);
+  const uint32_t sb_c = (tiles_c + 3u) / 4u, sbs = ((tiles_r + 3u) / 4u) * sb_c;
+  const uint32_t grid = (sbs + 7u) / 8u * 128u;
+  hipLaunchKernelGGL(pattern_2d_kernel, dim3(grid), dim3(kThreads), 0, st, reinterpret_cast<const uint16_t*>(x), rows,
+                     cols, (uint8_t*)codes_row, (uint8_t*)scales_row, (uint8_t*)codes_col, (uint8_t*)scales_col,
+                     tiles_c, sb_c, sbs);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
