@@ -155,7 +155,6 @@ mxq_status quantize_impl(const void* x, mxq_dtype dt, int64_t rows, int64_t cols
   a.sr_offset = sr_offset;
   a.total_rows = rows;
   a.total_cols = cols;
-  a.row0 = 0;
   a.codes_row = a.want_row ? codes_row : nullptr;
   a.scales_row = a.want_row ? scales_row : nullptr;
   a.codes_col = codes_col;

@@ -54,7 +54,6 @@ struct TileLaunch {
   uint32_t sign_mask;
   uint64_t sr_seed, sr_offset;
   int64_t total_rows, total_cols;  // of the whole tensor (SR indices)
-  int64_t row0;                    // first row of this slab in the whole tensor
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
   int64_t ld_col_codes, ld_col_scales;  // row strides of the column-wise outputs
   const float* amax;   // NVFP4: the tensor amax, or the tensor scale when st_given

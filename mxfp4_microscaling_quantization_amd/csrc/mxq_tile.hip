@@ -308,14 +308,12 @@ struct StripParams {
   const uint16_t* x;
   int64_t ldx;
   int64_t rows, cols;     // slab extent
-  int64_t total_rows;     // whole tensor (column-wise SR index and strides)
   int64_t row0;           // slab's first row in the whole tensor (a multiple of kFlushR)
   uint32_t strips;        // strips across the slab
   uint32_t flushes;       // flush units down the slab
   uint32_t per_wg;        // flush units per workgroup
   uint32_t units;         // workgroups down one strip
   uint32_t sign_mask;
-  uint64_t sr_seed, sr_offset;
   uint8_t *codes_row, *scales_row, *codes_col, *scales_col;
   int64_t ld_col_codes, ld_col_scales;
   const float* amax;
@@ -354,6 +352,7 @@ __device__ __forceinline__ uint32_t opaque_lane() {
 // for (128) fits every variant without spills.
 template <int FMT, int SR, bool RHT, bool ROW>
 __global__ __launch_bounds__(kTileThreads, 4) void quantize_strip_kernel(StripParams p) {
+  static_assert(SR == kRne, "the strip walk serves nearest-even rounding");
   constexpr int bs = FMT == kMX ? 32 : 16;
   constexpr int kChunksPerRow = kStripC / 8;                // 32 lanes per row
   constexpr int kRowStep = kTileThreads / kChunksPerRow;    // 8 rows between a thread's chunks
@@ -438,14 +437,9 @@ __global__ __launch_bounds__(kTileThreads, 4) void quantize_strip_kernel(StripPa
               float v[8];
               to_f32(rr, v);
               if constexpr (RHT) h16_pair(v, t & 1u);
-              uint32_t u[8];
-              if constexpr (SR != kRne) {
-                const uint64_t grow = (uint64_t)(p.row0 + r0 + row);
-                sr_values<SR, 8>(p.sr_offset + grow * cols + col, p.sr_seed, u);
-              }
               uint32_t byte, packed;
-              if constexpr (FMT == kMX) packed = mx_encode8<SR != kRne, RHT ? 2 : 0, !RHT>(v, u, byte);
-              else packed = nv_encode8<SR != kRne>(v, u, nt, byte);
+              if constexpr (FMT == kMX) packed = mx_encode8<false, RHT ? 2 : 0, !RHT>(v, nullptr, byte);
+              else packed = nv_encode8<false>(v, nullptr, nt, byte);
               if (row < nr && col_ok) {
                 *reinterpret_cast<uint32_t*>(crow + (uint64_t)(j * kRowStep) * (cols >> 1)) = packed;
                 if ((cc * 8) % bs == 0) rsc[row * 16 + (cc * 8) / bs] = (uint8_t)byte;
@@ -469,7 +463,6 @@ __global__ __launch_bounds__(kTileThreads, 4) void quantize_strip_kernel(StripPa
         const uint8_t* const rd = buf + (h * 32 * kStripC + (((int)(t >> 1)) ^ (32 * h))) * 2;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const int c = (int)(t >> 1) + 128 * m;
           float v[32];
 #pragma unroll
           for (int i = 0; i < 32; ++i)
@@ -478,17 +471,12 @@ __global__ __launch_bounds__(kTileThreads, 4) void quantize_strip_kernel(StripPa
             h16_local(v);
             h16_local(v + 16);
           }
-          uint32_t u[32];
-          if constexpr (SR != kRne) {
-            const uint64_t grow0 = (uint64_t)(p.row0 + r0 + h * 32);
-            sr_values<SR, 32>(p.sr_offset + (uint64_t)(c0 + c) * (uint64_t)p.total_rows + grow0, p.sr_seed, u);
-          }
           if constexpr (FMT == kMX) {
-            const uint32_t byte = mx_encode32<SR != kRne, RHT ? 2 : 0, !RHT>(v, u, acc[sq][m]);
+            const uint32_t byte = mx_encode32<false, RHT ? 2 : 0, !RHT>(v, nullptr, acc[sq][m]);
             scol[m][0] |= byte << (8 * sq);
           } else {
-            const uint32_t b0 = nv_encode16<SR != kRne>(v, u, nt, acc[sq][m]);
-            const uint32_t b1 = nv_encode16<SR != kRne>(v + 16, u + 16, nt, acc[sq][m] + 2);
+            const uint32_t b0 = nv_encode16<false>(v, nullptr, nt, acc[sq][m]);
+            const uint32_t b1 = nv_encode16<false>(v + 16, nullptr, nt, acc[sq][m] + 2);
             scol[m][sq >> 1] |= (b0 | (b1 << 8)) << (16 * (sq & 1));
           }
           // keep one task's values from being held across the next task's reads
@@ -561,8 +549,7 @@ static hipError_t launch_strips(const TileLaunch& a, hipStream_t st) {
     p.ldx = a.ldx;
     p.rows = nr;
     p.cols = a.cols;
-    p.total_rows = a.total_rows;
-    p.row0 = a.row0 + s0;
+    p.row0 = s0;
     p.strips = (uint32_t)strips;
     const int64_t flushes = (nr + kFlushR - 1) / kFlushR;
     p.flushes = (uint32_t)flushes;
@@ -570,8 +557,6 @@ static hipError_t launch_strips(const TileLaunch& a, hipStream_t st) {
     p.per_wg = (uint32_t)std::min<int64_t>(4, std::max<int64_t>(1, flushes * strips / 1024));
     p.units = (uint32_t)((flushes + p.per_wg - 1) / p.per_wg);
     p.sign_mask = a.sign_mask;
-    p.sr_seed = a.sr_seed;
-    p.sr_offset = a.sr_offset;
     const int bs = FMT == kMX ? 32 : 16;
     p.codes_row = a.codes_row ? a.codes_row + s0 * (a.cols / 2) : nullptr;
     p.scales_row = a.scales_row ? a.scales_row + s0 * (a.cols / bs) : nullptr;
@@ -596,47 +581,48 @@ static hipError_t launch_tiles_shape(const TileLaunch& a, hipStream_t st) {
   // rounding's random words and the NVFP4 row side need more registers than the
   // walk leaves for four resident workgroups per CU, and stay on tiles.
   if constexpr (sizeof(T) == 2 && SR == kRne && !(FMT == kNV && ROW)) {
-    if (a.row0 % kFlushR == 0) return launch_strips<FMT, SR, RHT, ROW>(a, st);
+    return launch_strips<FMT, SR, RHT, ROW>(a, st);
+  } else {
+    using Shape = TileShape<T, FMT, RHT, ROW>;
+    constexpr int kTileR = Shape::R, kTileC = Shape::C, kVGroup = Shape::V;
+    // slabs of at most 2^22 tiles (cols <= 2^30 gives at most 2^23 tiles per tile row)
+    const int64_t tiles_per_row = (a.cols + kTileC - 1) / kTileC;
+    const int64_t max_rows = (int64_t)kTileR * std::max<int64_t>(1, ((int64_t)1 << 22) / tiles_per_row);
+    for (int64_t s0 = 0; s0 < a.rows; s0 += max_rows) {
+      const int64_t nr = std::min(max_rows, a.rows - s0);
+      TileParams p;
+      const size_t esz = sizeof(T);
+      p.x = reinterpret_cast<const uint8_t*>(a.x) + (size_t)s0 * a.ldx * esz;
+      p.ldx = a.ldx;
+      p.rows = nr;
+      p.cols = a.cols;
+      p.total_rows = a.total_rows;
+      p.row0 = s0;
+      const int64_t tiles_r = (nr + kTileR - 1) / kTileR;
+      const int64_t tiles_c = (a.cols + kTileC - 1) / kTileC;
+      p.tiles_r = (uint32_t)tiles_r;
+      p.tiles_c = (uint32_t)tiles_c;
+      p.groups = (uint32_t)(((tiles_r + kVGroup - 1) / kVGroup) * tiles_c);
+      p.sign_mask = a.sign_mask;
+      p.sr_seed = a.sr_seed;
+      p.sr_offset = a.sr_offset;
+      const int bs = FMT == kMX ? 32 : 16;
+      p.codes_row = a.codes_row ? a.codes_row + s0 * (a.cols / 2) : nullptr;
+      p.scales_row = a.scales_row ? a.scales_row + s0 * (a.cols / bs) : nullptr;
+      p.codes_col = a.codes_col;
+      p.scales_col = a.scales_col;
+      p.ld_col_codes = a.ld_col_codes;
+      p.ld_col_scales = a.ld_col_scales;
+      p.amax = a.amax;
+      p.st_given = a.st_given ? 1 : 0;
+      p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
+      const uint32_t grid = 8u * kVGroup * ((p.groups + 7u) / 8u);
+      hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, ROW, true>), dim3(grid), dim3(kTileThreads), 0, st, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  using Shape = TileShape<T, FMT, RHT, ROW>;
-  constexpr int kTileR = Shape::R, kTileC = Shape::C, kVGroup = Shape::V;
-  // slabs of at most 2^22 tiles (cols <= 2^30 gives at most 2^23 tiles per tile row)
-  const int64_t tiles_per_row = (a.cols + kTileC - 1) / kTileC;
-  const int64_t max_rows = (int64_t)kTileR * std::max<int64_t>(1, ((int64_t)1 << 22) / tiles_per_row);
-  for (int64_t s0 = 0; s0 < a.rows; s0 += max_rows) {
-    const int64_t nr = std::min(max_rows, a.rows - s0);
-    TileParams p;
-    const size_t esz = sizeof(T);
-    p.x = reinterpret_cast<const uint8_t*>(a.x) + (size_t)s0 * a.ldx * esz;
-    p.ldx = a.ldx;
-    p.rows = nr;
-    p.cols = a.cols;
-    p.total_rows = a.total_rows;
-    p.row0 = a.row0 + s0;
-    const int64_t tiles_r = (nr + kTileR - 1) / kTileR;
-    const int64_t tiles_c = (a.cols + kTileC - 1) / kTileC;
-    p.tiles_r = (uint32_t)tiles_r;
-    p.tiles_c = (uint32_t)tiles_c;
-    p.groups = (uint32_t)(((tiles_r + kVGroup - 1) / kVGroup) * tiles_c);
-    p.sign_mask = a.sign_mask;
-    p.sr_seed = a.sr_seed;
-    p.sr_offset = a.sr_offset;
-    const int bs = FMT == kMX ? 32 : 16;
-    p.codes_row = a.codes_row ? a.codes_row + s0 * (a.cols / 2) : nullptr;
-    p.scales_row = a.scales_row ? a.scales_row + s0 * (a.cols / bs) : nullptr;
-    p.codes_col = a.codes_col;
-    p.scales_col = a.scales_col;
-    p.ld_col_codes = a.ld_col_codes;
-    p.ld_col_scales = a.ld_col_scales;
-    p.amax = a.amax;
-    p.st_given = a.st_given ? 1 : 0;
-    p.tensor_scale = s0 == 0 ? a.tensor_scale : nullptr;
-    const uint32_t grid = 8u * kVGroup * ((p.groups + 7u) / 8u);
-    hipLaunchKernelGGL((quantize_tile_kernel<T, FMT, SR, RHT, ROW, true>), dim3(grid), dim3(kTileThreads), 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
 }
 
 template <typename T, int FMT, int SR, bool RHT>
