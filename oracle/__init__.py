@@ -37,6 +37,7 @@ Parity status per function (what pins it is in tests/test_oracle_*.py):
   philox.element_r16_halves  pinned against rocRAND's word stream (half n mod 2 of
                        word n/2), a hand-worked vector from the known-answer words,
                        and uniformity / unbiased-rounding statistics
-  rht.sign_mask_from_seed  parity unpinned: the seed-to-signs mapping is a
-                       definition made here (the pages only say "random signs").
+  rht.sign_mask_from_seed  the seed-to-signs mapping is a definition made here
+                       (the pages only say "random signs"); pinned by the published
+                       word of seed 0 (mask 0xE8D5) and rocRAND's engine
 """

@@ -14,7 +14,8 @@ Readings:
      is orthonormal ("transformations orthogonales").
   H2 the 16 signs s_i are given by a 16-bit mask: bit i set means s_i = -1; mask 0
      is the deterministic H16. Deriving the mask from a seed is a separate helper
-     (sign_mask_from_seed; parity unpinned, the mapping is defined here).
+     (sign_mask_from_seed; the mapping is a definition made here, pinned by the
+     generator's published known-answer word for seed 0 and by rocRAND's engine).
   H3 y is kept in working precision and quantised without an intermediate bf16
      rounding; this oracle computes y in float64 (the pages fix no precision).
   H4 row-wise: chunks along columns; column-wise: chunks along rows (the transform
@@ -49,8 +50,10 @@ def signs_from_mask(mask: int) -> np.ndarray:
 
 def sign_mask_from_seed(seed: int) -> int:
     """Sign mask for a seed: bits 0..15 of word 0 of Philox4x32-10 with
-    key = (seed low 32 bits, seed high 32 bits) and counter 0. Parity unpinned:
-    this mapping is a definition made here."""
+    key = (seed low 32 bits, seed high 32 bits) and counter 0. The mapping is a
+    definition made here (the pages only ask for random signs); that this code
+    follows it is pinned by the first published Philox vector (seed 0 gives
+    0xE8D5) and by element 0 of rocRAND's engine for other seeds."""
     w = philox4x32_10(np.zeros((1, 4), dtype=np.uint32), seed)
     return int(w[0, 0]) & 0xFFFF
 
