@@ -3,18 +3,19 @@
 One step = one pass of the nine hot-path kernels, each over the synthetic workload
 of the configuration it is quoted on (shapes of the pages' models: DeepSeek-V3-like
 MoE with hidden 7168 and 256 experts; Llama-3.1-8B hidden 4096 / FFN 14336):
-  cfg2  16384 x 7168 bf16 MoE activations   mxfp4_quantize, mxfp4_dequantize
-  cfg3  65536 x 7168 FP8 token buffer       fp8_to_mxfp4, mxfp4_to_fp8
-        (256 experts, Dirichlet(0.5) split)
-  cfg4  8192 x 14336 bf16 gradients         rht_mxfp4_rowcol (random-sign H16, row-
-        (N(0,1e-3) + Student-t(3) noise)    and column-wise MXFP4 from one read)
-  cfg5  32768 x 4096 bf16 with outliers     nvfp4_amax, nvfp4_quantize_rne,
-                                            nvfp4_quantize_sr (Philox seed 7)
+  moe_16384x7168       bf16 MoE activations       mxfp4_quantize, mxfp4_dequantize
+  experts_65536x7168   FP8 token buffer           fp8_to_mxfp4, mxfp4_to_fp8
+                       (256 experts, Dirichlet(0.5) split)
+  grads_8192x14336     bf16 gradients             rht_mxfp4_rowcol (random-sign H16, row-
+                       (N(0,1e-3) + Student-t(3)  and column-wise MXFP4 from one read)
+                       noise)
+  outliers_32768x4096  bf16 with outliers         nvfp4_amax, nvfp4_quantize_rne,
+                                                  nvfp4_quantize_sr (Philox seed 7)
 `value` = algorithmic bytes of the step (inputs read + outputs written, as the
 method defines them) / the time of exactly `steps` steps. Each kernel is also timed
 alone (`per_kernel`), beside a streaming kernel that moves the same bytes in the
 same read/write mix (`stream_reference`: what that traffic reaches on this chip).
-Config 1 (1024 x 4096, 10.6 MB: launch-bound) is timed eagerly and from a HIP
+The small case small_1024x4096 (10.6 MB: launch-bound) is timed eagerly and from a HIP
 graph. After the step the rows beyond it are timed at their own workloads, with the
 fused-vs-unfused ablation of the FP8 <-> MXFP4 conversions; the CPU oracle is timed
 on row samples of the same workloads (one core, then a pool of processes). Prints
@@ -80,8 +81,8 @@ def load_workloads():
     from mxfp4_microscaling_quantization_amd import workloads as W
 
     t0 = time.perf_counter()
-    w = {"cfg1": W.mxfp4_rowwise_small(), "cfg2": W.mxfp4_rowwise_moe(), "cfg3": W.fp8_moe_experts(),
-         "cfg4": W.rht_gradients(), "cfg5": W.nvfp4_activations()}
+    w = {"small_1024x4096": W.mxfp4_rowwise_small(), "moe_16384x7168": W.mxfp4_rowwise_moe(), "experts_65536x7168": W.fp8_moe_experts(),
+         "grads_8192x14336": W.rht_gradients(), "outliers_32768x4096": W.nvfp4_activations()}
     print(f"[bench] workloads generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     return w
 
@@ -120,13 +121,13 @@ def build_step(wl, dev, sets: int):
     def e(*shape, dtype=u8):
         return torch.empty(shape, dtype=dtype, device=dev)
 
-    x2, x4, x5 = wl["cfg2"].x.to(dev), wl["cfg4"].x.to(dev), wl["cfg5"].x.to(dev)
-    q8, s128 = wl["cfg3"].q8.to(dev), wl["cfg3"].s128.to(dev)
+    x2, x4, x5 = wl["moe_16384x7168"].x.to(dev), wl["grads_8192x14336"].x.to(dev), wl["outliers_32768x4096"].x.to(dev)
+    q8, s128 = wl["experts_65536x7168"].q8.to(dev), wl["experts_65536x7168"].s128.to(dev)
     R2, C2 = x2.shape
     R3, C3 = q8.shape
     R4, C4 = x4.shape
     R5, C5 = x5.shape
-    seed4, seed5 = wl["cfg4"].rht_seed, wl["cfg5"].sr_seed
+    seed4, seed5 = wl["grads_8192x14336"].rht_seed, wl["outliers_32768x4096"].sr_seed
     S = []
     for k in range(sets):
         st = {"x2q": x2 if k == 0 else x2.clone(), "q8": q8 if k == 0 else q8.clone(), "s128": s128.clone(),
@@ -147,28 +148,28 @@ def build_step(wl, dev, sets: int):
     n2, n3, n4, n5 = R2 * C2, R3 * C3, R4 * C4, R5 * C5
     sh2, sh3, sh4, sh5 = f"{R2}x{C2}", f"{R3}x{C3}", f"{R4}x{C4}", f"{R5}x{C5}"
     ks = [
-        Kernel("mxfp4_quantize", "cfg2", sh2,
+        Kernel("mxfp4_quantize", "moe_16384x7168", sh2,
                lambda k: mxq.mxq_quantize(S[k]["x2q"], "mxfp4", "row", out=S[k]["qz"]),
                mx_bytes(n2), n2, (16, 4, 1), 2 * n2),
-        Kernel("mxfp4_dequantize", "cfg2", sh2,
+        Kernel("mxfp4_dequantize", "moe_16384x7168", sh2,
                lambda k: mxq.mxq_dequantize(S[k]["deq_in"].codes_row, S[k]["deq_in"].scales_row, "mxfp4",
                                             out=S[k]["yb"]),
                mx_bytes(n2), n2, (4, 16, 3), n2 // 2),
-        Kernel("fp8_to_mxfp4", "cfg3", sh3,
+        Kernel("fp8_to_mxfp4", "experts_65536x7168", sh3,
                lambda k: mxq.mxq_fp8_to_mxfp4(S[k]["q8"], S[k]["s128"], out=S[k]["c8"]),
                fp8_bytes(n3), n3, (16, 8, 1), n3),
-        Kernel("mxfp4_to_fp8", "cfg3", sh3,
+        Kernel("mxfp4_to_fp8", "experts_65536x7168", sh3,
                lambda k: mxq.mxq_mxfp4_to_fp8(S[k]["f8_in"][0], S[k]["f8_in"][1], out=S[k]["f8"]),
                fp8_bytes(n3), n3, (8, 16, 3), n3 // 2),
-        Kernel("rht_mxfp4_rowcol", "cfg4", sh4,
+        Kernel("rht_mxfp4_rowcol", "grads_8192x14336", sh4,
                lambda k: mxq.mxq_rht_quantize(S[k]["x4"], seed4, "mxfp4", "both", out=S[k]["rq"]),
                2 * n4 + 2 * (n4 // 2 + n4 // 32), n4, ("strip",), 2 * n4),
-        Kernel("nvfp4_amax", "cfg5", sh5,
+        Kernel("nvfp4_amax", "outliers_32768x4096", sh5,
                lambda k: mxq.mxq_amax(S[k]["x5a"], out=S[k]["amax"]), 2 * n5 + 4, n5, (16, 0, 1), 2 * n5),
-        Kernel("nvfp4_quantize_rne", "cfg5", sh5,
+        Kernel("nvfp4_quantize_rne", "outliers_32768x4096", sh5,
                lambda k: mxq.mxq_quantize(S[k]["x5n"], "nvfp4", "row", amax=S[k]["amax"], out=S[k]["nq"]),
                nv_bytes(n5), n5, (16, 4, 1), 2 * n5),
-        Kernel("nvfp4_quantize_sr", "cfg5", sh5,
+        Kernel("nvfp4_quantize_sr", "outliers_32768x4096", sh5,
                lambda k: mxq.mxq_quantize(S[k]["x5s"], "nvfp4", "row", "sr", sr_seed=seed5, amax=S[k]["amax"],
                                           out=S[k]["sq"]),
                nv_bytes(n5), n5, (16, 4, 1), 2 * n5),
@@ -369,9 +370,9 @@ def valu_probe(dev, reps: int = 5) -> dict:
 
 
 # ---------------------------------------------------------------------------
-# config 1, the rows beyond the step, the ablation
+# the small case, the rows beyond the step, the ablation
 
-def config1_report(wl, dev, reps: int, graph: bool = True) -> list:
+def small_case_report(wl, dev, reps: int, graph: bool = True) -> list:
     """1024 x 4096 (10.6 MB): 64 rotating buffer sets, eager launches and the same
     launches replayed from a captured HIP graph (device time without the host's
     per-call cost)."""
@@ -380,7 +381,7 @@ def config1_report(wl, dev, reps: int, graph: bool = True) -> list:
     from mxfp4_microscaling_quantization_amd import mxq
 
     n = 64
-    xs = [wl["cfg1"].x.to(dev) for _ in range(n)]
+    xs = [wl["small_1024x4096"].x.to(dev) for _ in range(n)]
     R, C = xs[0].shape
     N = R * C
     qs = [mxq.mxq_quantize(x, "mxfp4", "row") for x in xs]
@@ -415,11 +416,11 @@ def config1_report(wl, dev, reps: int, graph: bool = True) -> list:
         for k in range(n):
             fn(k)
         keep_busy(dev)
-        r = {"config": "cfg1", "kernel": name, "shape": f"{R}x{C}", "launch": "eager"}
+        r = {"config": "small_1024x4096", "kernel": name, "shape": f"{R}x{C}", "launch": "eager"}
         r.update(figures(avg_launch_us(fn, n, reps), mx_bytes(N), N))
         out.append(r)
         if graph:
-            r = {"config": "cfg1", "kernel": name, "shape": f"{R}x{C}", "launch": "hip_graph"}
+            r = {"config": "small_1024x4096", "kernel": name, "shape": f"{R}x{C}", "launch": "hip_graph"}
             r.update(figures(graph_us(fn), mx_bytes(N), N))
             out.append(r)
     del xs, qs, ys
@@ -430,9 +431,9 @@ def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[di
     """The rows beyond the step, each at its own workload with rotating input copies:
     NVFP4 amax + quantise as one call (the amax computed by the call), 16x16-scaled
     NVFP4 of a 14336 x 4096 FFN weight (both outputs), RHT + NVFP4 column-wise and
-    MXFP4 stochastic rounding of the cfg4 gradients, the MXFP4-rows -> FP8-columns
+    MXFP4 stochastic rounding of the 8192x14336 gradients, the MXFP4-rows -> FP8-columns
     conversion of the 65536 x 7168 token buffer of 256 experts; and the fused-vs-
-    unfused ablation of the FP8 <-> MXFP4 conversions on the cfg3 buffer."""
+    unfused ablation of the FP8 <-> MXFP4 conversions on the 65536x7168 token buffer."""
     import numpy as np
     import torch
 
@@ -457,17 +458,17 @@ def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[di
 
     n = 3
     # NVFP4 end to end: one call that computes the amax first (two passes over x)
-    x5 = [wl["cfg5"].x.to(dev) for _ in range(n)]
+    x5 = [wl["outliers_32768x4096"].x.to(dev) for _ in range(n)]
     R5, C5 = x5[0].shape
     N5 = R5 * C5
     o5 = [mxq.mxq_quantize(v, "nvfp4", "row") for v in x5]
-    row("nvfp4_amax_quantize_rne", "cfg5", f"{R5}x{C5}",
+    row("nvfp4_amax_quantize_rne", "outliers_32768x4096", f"{R5}x{C5}",
         lambda k: mxq.mxq_quantize(x5[k], "nvfp4", "row", out=o5[k]), n, nv_bytes(N5), N5,
         "amax pass + quantise pass in one call (NULL amax); bytes = the quantiser's in+out, "
         "so the two-pass ceiling is 2.5625 / 4.5625 of the HBM peak")
     a5 = [mxq.mxq_amax(v) for v in x5]
-    row("nvfp4_quantize_sr16", "cfg5", f"{R5}x{C5}",
-        lambda k: mxq.mxq_quantize(x5[k], "nvfp4", "row", "sr16", sr_seed=wl["cfg5"].sr_seed, amax=a5[k],
+    row("nvfp4_quantize_sr16", "outliers_32768x4096", f"{R5}x{C5}",
+        lambda k: mxq.mxq_quantize(x5[k], "nvfp4", "row", "sr16", sr_seed=wl["outliers_32768x4096"].sr_seed, amax=a5[k],
                                    out=o5[k]), n, nv_bytes(N5), N5,
         "NVFP4 stochastic rounding, opt-in 16-bit-halves random stream (one Philox call per 8 elements)")
     del x5, o5, a5
@@ -490,40 +491,40 @@ def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[di
         rows["nvfp4_2d_rowcol"]["stream_ref_pattern"] = "16x16 NVFP4 tile pattern, bytes only"
         print(f"[ref]   nvfp4_2d_rowcol {ref['GB_s']:8.1f} GB/s (16x16 NVFP4 tile pattern); kernel at "
               f"{100 * rows['nvfp4_2d_rowcol']['frac_of_stream_ref']:.1f}%", file=sys.stderr, flush=True)
-    # gradient recipes on the cfg4 tensor
-    x4 = [wl["cfg4"].x.to(dev) for _ in range(n)]
+    # gradient recipes on the grads_8192x14336 tensor
+    x4 = [wl["grads_8192x14336"].x.to(dev) for _ in range(n)]
     R4, C4 = x4[0].shape
     N4 = R4 * C4
-    mask = mxq.mxq_rht_signs(wl["cfg4"].rht_seed)
+    mask = mxq.mxq_rht_signs(wl["grads_8192x14336"].rht_seed)
     ra = [mxq.mxq_rht_amax(v, mask, "col") for v in x4]
-    rq = [mxq.mxq_rht_quantize(v, wl["cfg4"].rht_seed, "nvfp4", "col", amax=a) for v, a in zip(x4, ra)]
-    row("rht_nvfp4_col", "cfg4", f"{R4}x{C4}",
-        lambda k: mxq.mxq_rht_quantize(x4[k], wl["cfg4"].rht_seed, "nvfp4", "col", amax=ra[k], out=rq[k]), n,
+    rq = [mxq.mxq_rht_quantize(v, wl["grads_8192x14336"].rht_seed, "nvfp4", "col", amax=a) for v, a in zip(x4, ra)]
+    row("rht_nvfp4_col", "grads_8192x14336", f"{R4}x{C4}",
+        lambda k: mxq.mxq_rht_quantize(x4[k], wl["grads_8192x14336"].rht_seed, "nvfp4", "col", amax=ra[k], out=rq[k]), n,
         nv_bytes(N4), N4, "H16 along rows, column-wise NVFP4 (the wgrad recipe)")
-    row("rht_amax_col", "cfg4", f"{R4}x{C4}", lambda k: mxq.mxq_rht_amax(x4[k], mask, "col", out=ra[k]), n,
+    row("rht_amax_col", "grads_8192x14336", f"{R4}x{C4}", lambda k: mxq.mxq_rht_amax(x4[k], mask, "col", out=ra[k]), n,
         2 * N4 + 4, N4, "amax of the column-wise transform")
     del rq
     sq = [mxq.mxq_quantize(v, "mxfp4", "row") for v in x4]
-    row("mxfp4_quantize_sr", "cfg4", f"{R4}x{C4}",
+    row("mxfp4_quantize_sr", "grads_8192x14336", f"{R4}x{C4}",
         lambda k: mxq.mxq_quantize(x4[k], "mxfp4", "row", "sr", sr_seed=7, out=sq[k]), n, mx_bytes(N4), N4,
         "row-wise MXFP4, Philox stochastic rounding (gradients)")
-    row("mxfp4_quantize_sr16", "cfg4", f"{R4}x{C4}",
+    row("mxfp4_quantize_sr16", "grads_8192x14336", f"{R4}x{C4}",
         lambda k: mxq.mxq_quantize(x4[k], "mxfp4", "row", "sr16", sr_seed=7, out=sq[k]), n, mx_bytes(N4), N4,
         "row-wise MXFP4, stochastic rounding with the opt-in 16-bit-halves stream")
     rcol = [(torch.empty((C4, R4 // 2), dtype=torch.uint8, device=dev),
              torch.empty((C4, R4 // 32), dtype=torch.uint8, device=dev)) for _ in range(n)]
-    row("mxfp4_rowcol_no_rht", "cfg4", f"{R4}x{C4}",
+    row("mxfp4_rowcol_no_rht", "grads_8192x14336", f"{R4}x{C4}",
         lambda k: mxq.mxq_quantize(x4[k], "mxfp4", "both", out=mxq.Quantized(sq[k].codes_row, sq[k].scales_row,
                                                                               rcol[k][0], rcol[k][1], None)),
         n, 2 * N4 + 2 * (N4 // 2 + N4 // 32), N4, "the fused row + column kernel without the transform")
     del x4, ra, sq, rcol
     torch.cuda.empty_cache()
 
-    # ---- fused vs unfused on the cfg3 buffer (the pages' kernel-level claim)
+    # ---- fused vs unfused on the experts_65536x7168 buffer (the pages' kernel-level claim)
     abl = {}
     n = 2
-    q8 = [wl["cfg3"].q8.to(dev) for _ in range(n)]
-    s128 = [wl["cfg3"].s128.to(dev) for _ in range(n)]
+    q8 = [wl["experts_65536x7168"].q8.to(dev) for _ in range(n)]
+    s128 = [wl["experts_65536x7168"].s128.to(dev) for _ in range(n)]
     R3, C3 = q8[0].shape
     N3 = R3 * C3
     f_out = [mxq.mxq_fp8_to_mxfp4(q8[k], s128[k]) for k in range(n)]
@@ -538,9 +539,9 @@ def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[di
 
     fb = fp8_bytes(N3)
     ideal = (N3 + 4 * (N3 // 128) + 2 * N3 + 2 * N3 + N3 // 2 + N3 // 32) / fb
-    t_f = row("fp8_to_mxfp4 (fused)", "cfg3", f"{R3}x{C3}",
+    t_f = row("fp8_to_mxfp4 (fused)", "experts_65536x7168", f"{R3}x{C3}",
               lambda k: mxq.mxq_fp8_to_mxfp4(q8[k], s128[k], out=f_out[k]), n, fb, N3, "E4M3 + 1x128 scales")
-    t_u = row("fp8_to_mxfp4 (unfused)", "cfg3", f"{R3}x{C3}", fp8_unfused, n, fb, N3,
+    t_u = row("fp8_to_mxfp4 (unfused)", "experts_65536x7168", f"{R3}x{C3}", fp8_unfused, n, fb, N3,
               "torch E4M3->bf16 cast and scaling, then mxq_quantize")
     u = fp8_unfused(0)
     torch.cuda.synchronize()
@@ -558,9 +559,9 @@ def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[di
         q8o[k].copy_(q.view(torch.uint8).view(R3, C3))
         return q8o[k], sc
 
-    t_f = row("mxfp4_to_fp8 (fused)", "cfg3", f"{R3}x{C3}", lambda k: mxq.mxq_mxfp4_to_fp8(*f_out[k], out=b_out[k]),
+    t_f = row("mxfp4_to_fp8 (fused)", "experts_65536x7168", f"{R3}x{C3}", lambda k: mxq.mxq_mxfp4_to_fp8(*f_out[k], out=b_out[k]),
               n, fb, N3, "MXFP4 -> E4M3 + 1x128 scales")
-    t_u = row("mxfp4_to_fp8 (unfused)", "cfg3", f"{R3}x{C3}", mx_unfused, n, fb, N3,
+    t_u = row("mxfp4_to_fp8 (unfused)", "experts_65536x7168", f"{R3}x{C3}", mx_unfused, n, fb, N3,
               "mxq_dequantize to bf16, then torch scaling and E4M3 cast")
     uq, us_ = mx_unfused(0)
     torch.cuda.synchronize()
@@ -580,16 +581,16 @@ def extra_rows(wl, dev, reps: int, traffic: dict, refs: bool = True) -> tuple[di
     outs = [mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off) for k in range(n)]
     outs = [(o[0].as_strided((Cb, Rb), (o[0].stride(0), 1)), o[1]) for o in outs]
     G = int(np.sum((np.diff(w.offsets) + 127) // 128))
-    row("fp4_row_to_fp8_col", "cfg3", f"{Rb}x{Cb}",
+    row("fp4_row_to_fp8_col", "experts_65536x7168", f"{Rb}x{Cb}",
         lambda k: mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off, out=outs[k]), n,
         Nb // 2 + Nb // 32 + Nb + 4 * Cb * G + 8 * len(w.offsets), Nb,
-        f"MXFP4 tokens of 256 experts (the cfg3 split) -> E4M3 of the transpose, {G} groups of 128 tokens")
+        f"MXFP4 tokens of 256 experts (the split of the 65536x7168 buffer) -> E4M3 of the transpose, {G} groups of 128 tokens")
     # the same buffer split into 256 experts of 256 tokens: every group starts on a
     # 128-byte output line (how much of the time the ragged split's unaligned group
     # runs cost)
     off_al = torch.arange(0, Rb + 1, Rb // 256, dtype=torch.int64, device=dev)
     G_al = Rb // 128
-    row("fp4_row_to_fp8_col_aligned_experts", "cfg3", f"{Rb}x{Cb}",
+    row("fp4_row_to_fp8_col_aligned_experts", "experts_65536x7168", f"{Rb}x{Cb}",
         lambda k: mxq.mxq_fp4_row_to_fp8_col(codes[k], e8[k], off_al, out=outs[k]), n,
         Nb // 2 + Nb // 32 + Nb + 4 * Cb * G_al + 8 * 257, Nb,
         "the same buffer as 256 experts of 256 tokens (every group line-aligned): the cost of unaligned experts")
@@ -658,12 +659,12 @@ def cpu_baseline(wl, rows: tuple, pool_size: int) -> dict | None:
     r2, r3, r4, r5 = rows
     _CPU["rows"] = rows
     f64 = lambda t: t.float().double().numpy()  # noqa: E731
-    _CPU["x2"] = f64(wl["cfg2"].x)
-    _CPU["q8"] = wl["cfg3"].q8.numpy()
-    _CPU["s3"] = wl["cfg3"].s128.numpy().view(np.uint32)
-    _CPU["x4"] = f64(wl["cfg4"].x)
-    _CPU["x5"] = f64(wl["cfg5"].x)
-    _CPU["mask"] = orht.sign_mask_from_seed(wl["cfg4"].rht_seed)
+    _CPU["x2"] = f64(wl["moe_16384x7168"].x)
+    _CPU["q8"] = wl["experts_65536x7168"].q8.numpy()
+    _CPU["s3"] = wl["experts_65536x7168"].s128.numpy().view(np.uint32)
+    _CPU["x4"] = f64(wl["grads_8192x14336"].x)
+    _CPU["x5"] = f64(wl["outliers_32768x4096"].x)
+    _CPU["mask"] = orht.sign_mask_from_seed(wl["grads_8192x14336"].rht_seed)
     t0 = time.perf_counter()
     nb1 = _oracle_step(0)
     t1 = time.perf_counter() - t0
@@ -678,8 +679,8 @@ def cpu_baseline(wl, rows: tuple, pool_size: int) -> dict | None:
     except OSError:
         pass
     res = {"value": round(single, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "cpu_model": model,
-           "sample": f"the nine kernels' oracle counterparts on rows of each workload ({r2} of cfg2, {r3} of cfg3, "
-                     f"{r4} of cfg4, {r5} of cfg5), {t1:.1f} s, one process (numpy elementwise is single-threaded)"}
+           "sample": f"the nine kernels' oracle counterparts on rows of each workload ({r2} of moe_16384x7168, {r3} of experts_65536x7168, "
+                     f"{r4} of grads_8192x14336, {r5} of outliers_32768x4096), {t1:.1f} s, one process (numpy elementwise is single-threaded)"}
     if pool_size > 1:
         ctx = mp.get_context("fork")
         with ctx.Pool(pool_size) as pool:
@@ -692,7 +693,7 @@ def cpu_baseline(wl, rows: tuple, pool_size: int) -> dict | None:
         res.update({"value": round(pooled, 4), "cores": pool_size,
                     "sample": f"the nine kernels' oracle counterparts, {pool_size} processes (multiprocessing "
                               f"pool, one per core of the affinity mask, at most 16), each on its own window of "
-                              f"rows of each workload ({r2} of cfg2, {r3} of cfg3, {r4} of cfg4, {r5} of cfg5; "
+                              f"rows of each workload ({r2} of moe_16384x7168, {r3} of experts_65536x7168, {r4} of grads_8192x14336, {r5} of outliers_32768x4096; "
                               f"windows wrap where the pool covers more than a tensor), {tp:.1f} s"})
     _CPU.clear()
     return res
@@ -836,9 +837,9 @@ def main() -> int:
     if valu_ref:
         valu["probe"] = valu_ref
 
-    config1 = config1_report(wl, dev, args.kernel_reps, graph=not args.no_graph)
-    for r in config1:
-        print(f"[cfg1]  {r['kernel']:18s} {r['launch']:9s} {r['us']:8.2f} us  {100 * r['frac_hbm_peak']:5.1f}%",
+    small = small_case_report(wl, dev, args.kernel_reps, graph=not args.no_graph)
+    for r in small:
+        print(f"[small_1024x4096]  {r['kernel']:18s} {r['launch']:9s} {r['us']:8.2f} us  {100 * r['frac_hbm_peak']:5.1f}%",
               file=sys.stderr, flush=True)
 
     nxt, abl = (None, None)
@@ -860,14 +861,14 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "mxfp4_nvfp4_hot_path_per_config: the nine quantise/convert kernels per step, each "
-                               "on its configuration's workload (cfg2 16384x7168 bf16 MoE activations; cfg3 "
-                               "65536x7168 FP8 tokens of 256 experts; cfg4 8192x14336 bf16 gradients; cfg5 "
-                               "32768x4096 bf16 with outliers)",
+        "config": {"workload": "mxfp4_nvfp4_hot_path_per_workload: the nine quantise/convert kernels per step, "
+                               "each on its own workload (moe_16384x7168: bf16 MoE activations; experts_65536x7168: "
+                               "FP8 tokens of 256 experts; grads_8192x14336: bf16 gradients; outliers_32768x4096: "
+                               "bf16 with outliers)",
                    "bytes_per_step": step_bytes, "elements_per_step": sum(elements.values())},
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "per_kernel": per,
-        "config1": config1,
+        "small_case": small,
         "roofline": roof,
         "valu": valu or None,
         "stream_reference": refs,
