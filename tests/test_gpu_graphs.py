@@ -1,9 +1,10 @@
 """The entry points under HIP graph capture (every kernel family: row-wise, strip and
 tile column-wise, 16x16 NVFP4, FP8 conversions, rows -> FP8 columns): the library
 launches only kernels (the amax target is cleared by a small fill kernel, not a
-memset), so a caller can capture a sequence of calls once and replay it. The graph is replayed several times with new
-data copied into its static inputs, with eager work and synchronisations between the
-replays, and every replay is compared with eager calls on the same data."""
+memset), so a caller can capture a sequence of calls once and replay it. The graph
+is replayed several times with new data copied into its static inputs, with eager
+work and synchronisations between the replays, and every replay is compared with
+eager calls on the same data."""
 import numpy as np
 import pytest
 import torch
