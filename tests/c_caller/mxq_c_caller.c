@@ -1,0 +1,92 @@
+/*
+ * A plain C caller of libmxq: no PyTorch and no Python binding, only include/mxq.h and
+ * the HIP runtime. It reads a row-major bf16 tensor [rows, cols] from a file, copies it
+ * to device memory from hipMalloc, quantises it to MXFP4 row- and column-wise in one
+ * call (nearest even), dequantises the row-wise codes back to bf16, and writes every
+ * output to <prefix>.codes_row, .scales_row, .codes_col, .scales_col and .deq_row.
+ *
+ * usage: mxq_c_caller rows cols input.bin prefix     (rows % 32 == 0, cols % 32 == 0)
+ * Exit status: 0 on success, 1 on a usage or I/O error, 2 on a library or HIP error.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "mxq.h"
+
+static int hip_ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return 1;
+  fprintf(stderr, "%s: %s\n", what, hipGetErrorString(e));
+  return 0;
+}
+
+static int write_file(const char* prefix, const char* ext, const void* p, size_t n) {
+  char path[4096];
+  snprintf(path, sizeof path, "%s.%s", prefix, ext);
+  FILE* f = fopen(path, "wb");
+  if (!f) return 0;
+  const size_t w = fwrite(p, 1, n, f);
+  fclose(f);
+  return w == n;
+}
+
+int main(int argc, char** argv) {
+  if (argc != 5) {
+    fprintf(stderr, "usage: %s rows cols input.bin prefix\n", argv[0]);
+    return 1;
+  }
+  const int64_t rows = atoll(argv[1]), cols = atoll(argv[2]);
+  if (rows <= 0 || cols <= 0 || rows % 32 || cols % 32) {
+    fprintf(stderr, "rows and cols must be positive multiples of 32\n");
+    return 1;
+  }
+  const size_t n = (size_t)rows * (size_t)cols;
+  const size_t sizes[5] = {n * 2, n / 2, n / 32, n / 2, n / 32};  /* x, codes/scales row, codes/scales col */
+  uint8_t* host[5];
+  for (int i = 0; i < 5; ++i) host[i] = (uint8_t*)malloc(sizes[i]);
+  uint16_t* deq = (uint16_t*)malloc(n * 2);
+  FILE* f = fopen(argv[3], "rb");
+  if (!f || fread(host[0], 1, sizes[0], f) != sizes[0]) {
+    fprintf(stderr, "cannot read %zu bytes from %s\n", sizes[0], argv[3]);
+    return 1;
+  }
+  fclose(f);
+
+  void* dev[5] = {0, 0, 0, 0, 0};
+  void* ddeq = 0;
+  int ok = 1;
+  for (int i = 0; i < 5 && ok; ++i) ok = hip_ok(hipMalloc(&dev[i], sizes[i]), "hipMalloc");
+  if (ok) ok = hip_ok(hipMalloc(&ddeq, n * 2), "hipMalloc");
+  if (ok) ok = hip_ok(hipMemcpy(dev[0], host[0], sizes[0], hipMemcpyHostToDevice), "hipMemcpy in");
+  if (ok) {
+    /* a null stream: the device's default stream */
+    mxq_status s = mxq_quantize(dev[0], MXQ_BF16, rows, cols, cols, MXQ_MXFP4, MXQ_BOTH, MXQ_RNE, 0, 0,
+                                (uint8_t*)dev[1], (uint8_t*)dev[2], (uint8_t*)dev[3], (uint8_t*)dev[4], NULL,
+                                NULL, NULL);
+    if (s == MXQ_OK)
+      s = mxq_dequantize((const uint8_t*)dev[1], (const uint8_t*)dev[2], MXQ_MXFP4, rows, cols, NULL, ddeq,
+                         MXQ_BF16, NULL);
+    if (s != MXQ_OK) {
+      fprintf(stderr, "libmxq: %s\n", mxq_status_string(s));
+      ok = 0;
+    }
+  }
+  if (ok) ok = hip_ok(hipDeviceSynchronize(), "kernels");
+  for (int i = 1; i < 5 && ok; ++i) ok = hip_ok(hipMemcpy(host[i], dev[i], sizes[i], hipMemcpyDeviceToHost), "hipMemcpy out");
+  if (ok) ok = hip_ok(hipMemcpy(deq, ddeq, n * 2, hipMemcpyDeviceToHost), "hipMemcpy out");
+  for (int i = 0; i < 5; ++i)
+    if (dev[i]) hipFree(dev[i]);
+  if (ddeq) hipFree(ddeq);
+  if (!ok) return 2;
+
+  const char* ext[5] = {"", "codes_row", "scales_row", "codes_col", "scales_col"};
+  for (int i = 1; i < 5; ++i)
+    if (!write_file(argv[4], ext[i], host[i], sizes[i])) return 1;
+  if (!write_file(argv[4], "deq_row", deq, n * 2)) return 1;
+  for (int i = 0; i < 5; ++i) free(host[i]);
+  free(deq);
+  printf("ok %lld x %lld\n", (long long)rows, (long long)cols);
+  return 0;
+}

@@ -1,0 +1,62 @@
+"""The C ABI from a plain C program: tests/c_caller/mxq_c_caller.c is compiled with
+gcc against include/mxq.h and the HIP runtime (no PyTorch, no Python binding), reads
+a seeded bf16 tensor from a file into memory from hipMalloc, quantises it to MXFP4
+row- and column-wise in one call and dequantises the rows; every output is compared
+with the oracle bit for bit."""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_equal_bits, require_gpu
+from mxfp4_microscaling_quantization_amd import workloads
+from oracle import mx
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "mxfp4_microscaling_quantization_amd")
+SRC = os.path.join(ROOT, "tests", "c_caller", "mxq_c_caller.c")
+ROCM = "/opt/rocm"
+
+
+def build(tmp):
+    lib = os.path.join(PKG, "libmxq.so")
+    assert os.path.exists(lib), "libmxq.so is not built"
+    cc = shutil.which("gcc") or shutil.which("cc")
+    assert cc, "no C compiler"
+    exe = os.path.join(tmp, "mxq_c_caller")
+    subprocess.run([cc, "-std=c99", "-O1", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), SRC, "-o", exe,
+                    "-L", PKG, "-lmxq", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+                    f"-Wl,-rpath,{PKG}", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"],
+                   check=True, capture_output=True, text=True)
+    return exe
+
+
+@pytest.mark.parametrize("rows,cols", [(96, 544), (1024, 4096)])
+def test_c_program_matches_oracle(tmp_path, rows, cols):
+    require_gpu()
+    exe = build(str(tmp_path))
+    x = workloads.moe_activations(rows, cols, 21).cpu().contiguous()  # bf16
+    src = os.path.join(str(tmp_path), "x.bin")
+    x.view(torch.int16).numpy().tofile(src)
+    prefix = os.path.join(str(tmp_path), "out")
+    print(f"C caller {rows}x{cols}", flush=True)
+    r = subprocess.run([exe, str(rows), str(cols), src, prefix], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    got = {k: np.fromfile(f"{prefix}.{k}", dtype=np.uint8)
+           for k in ("codes_row", "scales_row", "codes_col", "scales_col")}
+    deq = np.fromfile(f"{prefix}.deq_row", dtype=np.uint16)
+
+    xf = x.float().numpy().astype(np.float64)
+    ref_c, ref_s = mx.mxfp4_quantize_rowwise(xf)
+    ref_cc, ref_sc = mx.mxfp4_quantize_colwise(xf)
+    assert_equal_bits(got["codes_row"].reshape(rows, cols // 2), ref_c, "C caller: row codes")
+    assert_equal_bits(got["scales_row"].reshape(rows, cols // 32), ref_s, "C caller: row scales")
+    assert_equal_bits(got["codes_col"].reshape(cols, rows // 2), ref_cc, "C caller: column codes")
+    assert_equal_bits(got["scales_col"].reshape(cols, rows // 32), ref_sc, "C caller: column scales")
+    assert_equal_bits(deq.reshape(rows, cols), mx.mxfp4_dequantize(ref_c, ref_s, "bf16"), "C caller: dequantised rows")
