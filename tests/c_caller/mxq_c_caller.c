@@ -45,14 +45,18 @@ int main(int argc, char** argv) {
   const size_t n = (size_t)rows * (size_t)cols;
   const size_t sizes[5] = {n * 2, n / 2, n / 32, n / 2, n / 32};  /* x, codes/scales row, codes/scales col */
   uint8_t* host[5];
-  for (int i = 0; i < 5; ++i) host[i] = (uint8_t*)malloc(sizes[i]);
+  int have = 1;
+  for (int i = 0; i < 5; ++i) have &= (host[i] = (uint8_t*)malloc(sizes[i])) != NULL;
   uint16_t* deq = (uint16_t*)malloc(n * 2);
-  FILE* f = fopen(argv[3], "rb");
-  if (!f || fread(host[0], 1, sizes[0], f) != sizes[0]) {
+  FILE* f = have && deq ? fopen(argv[3], "rb") : NULL;
+  const int read_ok = f && fread(host[0], 1, sizes[0], f) == sizes[0];
+  if (f) fclose(f);
+  if (!read_ok) {
     fprintf(stderr, "cannot read %zu bytes from %s\n", sizes[0], argv[3]);
+    for (int i = 0; i < 5; ++i) free(host[i]);
+    free(deq);
     return 1;
   }
-  fclose(f);
 
   void* dev[5] = {0, 0, 0, 0, 0};
   void* ddeq = 0;
@@ -79,14 +83,14 @@ int main(int argc, char** argv) {
   for (int i = 0; i < 5; ++i)
     if (dev[i]) hipFree(dev[i]);
   if (ddeq) hipFree(ddeq);
-  if (!ok) return 2;
 
+  int status = ok ? 0 : 2;
   const char* ext[5] = {"", "codes_row", "scales_row", "codes_col", "scales_col"};
-  for (int i = 1; i < 5; ++i)
-    if (!write_file(argv[4], ext[i], host[i], sizes[i])) return 1;
-  if (!write_file(argv[4], "deq_row", deq, n * 2)) return 1;
+  for (int i = 1; i < 5 && status == 0; ++i)
+    if (!write_file(argv[4], ext[i], host[i], sizes[i])) status = 1;
+  if (status == 0 && !write_file(argv[4], "deq_row", deq, n * 2)) status = 1;
   for (int i = 0; i < 5; ++i) free(host[i]);
   free(deq);
-  printf("ok %lld x %lld\n", (long long)rows, (long long)cols);
-  return 0;
+  if (status == 0) printf("ok %lld x %lld\n", (long long)rows, (long long)cols);
+  return status;
 }
