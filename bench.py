@@ -818,7 +818,7 @@ def main() -> int:
     d = per[dom]
     roof = {"kernel": dom, "bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": d["frac_hbm_peak"], "traffic": d["hbm_traffic_bytes"], "bytes_per_launch": d["bytes"],
-            "avg_launch_us": d["us"], "workload": f"{d['config']} {d['shape']}",
+            "avg_launch_us": d["us"], "workload": d["config"],
             "stream_ref_GB_s": d.get("stream_ref_GB_s")}
 
     # VALU issue analysis of the stochastic-rounding kernels from committed SQ counters
