@@ -2,8 +2,10 @@
  * A plain C caller of libmxq: no PyTorch and no Python binding, only include/mxq.h and
  * the HIP runtime. It reads a row-major bf16 tensor [rows, cols] from a file, copies it
  * to device memory from hipMalloc, quantises it to MXFP4 row- and column-wise in one
- * call (nearest even), dequantises the row-wise codes back to bf16, and writes every
- * output to <prefix>.codes_row, .scales_row, .codes_col, .scales_col and .deq_row.
+ * call (nearest even), dequantises the row-wise codes back to bf16, quantises it to
+ * NVFP4 row-wise with no amax given (the library computes the tensor amax and s_t),
+ * and writes every output to <prefix>.codes_row, .scales_row, .codes_col,
+ * .scales_col, .deq_row, .nv_codes, .nv_scales and .nv_st.
  *
  * usage: mxq_c_caller rows cols input.bin prefix     (rows % 32 == 0, cols % 32 == 0)
  * Exit status: 0 on success, 1 on a usage or I/O error, 2 on a library or HIP error.
@@ -60,9 +62,14 @@ int main(int argc, char** argv) {
 
   void* dev[5] = {0, 0, 0, 0, 0};
   void* ddeq = 0;
+  void* dnv[3] = {0, 0, 0};  /* NVFP4 codes, block scales, tensor scale */
+  const size_t nv_sizes[3] = {n / 2, n / 16, sizeof(float)};
+  uint8_t* nv_host[3] = {0, 0, 0};
   int ok = 1;
   for (int i = 0; i < 5 && ok; ++i) ok = hip_ok(hipMalloc(&dev[i], sizes[i]), "hipMalloc");
   if (ok) ok = hip_ok(hipMalloc(&ddeq, n * 2), "hipMalloc");
+  for (int i = 0; i < 3 && ok; ++i) ok = hip_ok(hipMalloc(&dnv[i], nv_sizes[i]), "hipMalloc");
+  for (int i = 0; i < 3 && ok; ++i) ok = (nv_host[i] = (uint8_t*)malloc(nv_sizes[i])) != NULL;
   if (ok) ok = hip_ok(hipMemcpy(dev[0], host[0], sizes[0], hipMemcpyHostToDevice), "hipMemcpy in");
   if (ok) {
     /* a null stream: the device's default stream */
@@ -72,6 +79,10 @@ int main(int argc, char** argv) {
     if (s == MXQ_OK)
       s = mxq_dequantize((const uint8_t*)dev[1], (const uint8_t*)dev[2], MXQ_MXFP4, rows, cols, NULL, ddeq,
                          MXQ_BF16, NULL);
+    /* amax NULL: the tensor amax is computed into the tensor-scale slot first */
+    if (s == MXQ_OK)
+      s = mxq_quantize(dev[0], MXQ_BF16, rows, cols, cols, MXQ_NVFP4, MXQ_ROWWISE, MXQ_RNE, 0, 0,
+                       (uint8_t*)dnv[0], (uint8_t*)dnv[1], NULL, NULL, NULL, (float*)dnv[2], NULL);
     if (s != MXQ_OK) {
       fprintf(stderr, "libmxq: %s\n", mxq_status_string(s));
       ok = 0;
@@ -80,15 +91,23 @@ int main(int argc, char** argv) {
   if (ok) ok = hip_ok(hipDeviceSynchronize(), "kernels");
   for (int i = 1; i < 5 && ok; ++i) ok = hip_ok(hipMemcpy(host[i], dev[i], sizes[i], hipMemcpyDeviceToHost), "hipMemcpy out");
   if (ok) ok = hip_ok(hipMemcpy(deq, ddeq, n * 2, hipMemcpyDeviceToHost), "hipMemcpy out");
+  for (int i = 0; i < 3 && ok; ++i)
+    ok = hip_ok(hipMemcpy(nv_host[i], dnv[i], nv_sizes[i], hipMemcpyDeviceToHost), "hipMemcpy out");
   for (int i = 0; i < 5; ++i)
     if (dev[i]) hipFree(dev[i]);
   if (ddeq) hipFree(ddeq);
+  for (int i = 0; i < 3; ++i)
+    if (dnv[i]) hipFree(dnv[i]);
 
   int status = ok ? 0 : 2;
   const char* ext[5] = {"", "codes_row", "scales_row", "codes_col", "scales_col"};
   for (int i = 1; i < 5 && status == 0; ++i)
     if (!write_file(argv[4], ext[i], host[i], sizes[i])) status = 1;
   if (status == 0 && !write_file(argv[4], "deq_row", deq, n * 2)) status = 1;
+  const char* nv_ext[3] = {"nv_codes", "nv_scales", "nv_st"};
+  for (int i = 0; i < 3 && status == 0; ++i)
+    if (!write_file(argv[4], nv_ext[i], nv_host[i], nv_sizes[i])) status = 1;
+  for (int i = 0; i < 3; ++i) free(nv_host[i]);
   for (int i = 0; i < 5; ++i) free(host[i]);
   free(deq);
   if (status == 0) printf("ok %lld x %lld\n", (long long)rows, (long long)cols);

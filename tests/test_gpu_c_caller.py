@@ -1,8 +1,9 @@
 """The C ABI from a plain C program: tests/c_caller/mxq_c_caller.c is compiled with
 gcc against include/mxq.h and the HIP runtime (no PyTorch, no Python binding), reads
 a seeded bf16 tensor from a file into memory from hipMalloc, quantises it to MXFP4
-row- and column-wise in one call and dequantises the rows; every output is compared
-with the oracle bit for bit."""
+row- and column-wise in one call, dequantises the rows, and quantises it to NVFP4
+with no amax given (the library computes the tensor amax first); every output is
+compared with the oracle bit for bit."""
 import os
 import shutil
 import subprocess
@@ -13,7 +14,7 @@ import torch
 
 from gpu_helpers import assert_equal_bits, require_gpu
 from mxfp4_microscaling_quantization_amd import workloads
-from oracle import mx
+from oracle import mx, nvfp4
 
 pytestmark = pytest.mark.gpu
 
@@ -60,3 +61,9 @@ def test_c_program_matches_oracle(tmp_path, rows, cols):
     assert_equal_bits(got["codes_col"].reshape(cols, rows // 2), ref_cc, "C caller: column codes")
     assert_equal_bits(got["scales_col"].reshape(cols, rows // 32), ref_sc, "C caller: column scales")
     assert_equal_bits(deq.reshape(rows, cols), mx.mxfp4_dequantize(ref_c, ref_s, "bf16"), "C caller: dequantised rows")
+    nv_c, nv_s, st = nvfp4.nvfp4_quantize_rowwise(xf)  # amax computed from x
+    assert np.fromfile(f"{prefix}.nv_st", dtype=np.float32)[0].view(np.uint32) == np.float32(st).view(np.uint32)
+    assert_equal_bits(np.fromfile(f"{prefix}.nv_scales", dtype=np.uint8).reshape(rows, cols // 16), nv_s,
+                      "C caller: NVFP4 block scales (NULL amax)")
+    assert_equal_bits(np.fromfile(f"{prefix}.nv_codes", dtype=np.uint8).reshape(rows, cols // 2), nv_c,
+                      "C caller: NVFP4 codes (NULL amax)")
