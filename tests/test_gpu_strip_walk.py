@@ -3,10 +3,9 @@
 bf16 inputs with nearest-even rounding go through the strip kernel (256-column
 strips walked in 256-row units, several units per workgroup on large tensors); fp32
 inputs and stochastic rounding go through the tile kernel, which the oracle pins on
-every variant (test_gpu_tile_matrix,
-test_gpu_rht_matrix). Both compute from fp32 values, so a bf16 tensor and its exact
-fp32 widening must give identical bits on every output, for every format, rounding,
-transform and axis. The shapes give one, two and four units per workgroup, a last
+every variant (test_gpu_tile_matrix, test_gpu_rht_matrix). Both compute from fp32
+values, so a bf16 tensor and its exact fp32 widening must give identical bits on
+every output, for every format, rounding, transform and axis. The shapes give one, two and four units per workgroup, a last
 unit of 32 to 96 rows, a last strip of 8 columns and (NVFP4) a last 32-row group
 with 16 rows. Compared on the device.
 """
