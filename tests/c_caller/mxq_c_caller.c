@@ -5,9 +5,13 @@
  * call (nearest even), dequantises the row-wise codes back to bf16, quantises it to
  * NVFP4 row-wise with no amax given (the library computes the tensor amax and s_t),
  * and writes every output to <prefix>.codes_row, .scales_row, .codes_col,
- * .scales_col, .deq_row, .nv_codes, .nv_scales and .nv_st.
+ * .scales_col, .deq_row, .nv_codes, .nv_scales and .nv_st. Given token offsets of
+ * experts (offsets[0] = 0, ..., offsets[E] = rows), it also converts the MXFP4 rows
+ * to FP8 columns per 128-token expert group: <prefix>.fc_q8 (E4M3 [cols, ld_q8],
+ * ld_q8 = rows rounded up to 16) and .fc_s (fp32 [cols, (rows + 127 E) / 128]).
  *
- * usage: mxq_c_caller rows cols input.bin prefix     (rows % 32 == 0, cols % 32 == 0)
+ * usage: mxq_c_caller rows cols input.bin prefix [offsets...]
+ *        (rows % 32 == 0, cols % 32 == 0)
  * Exit status: 0 on success, 1 on a usage or I/O error, 2 on a library or HIP error.
  */
 #include <stdint.h>
@@ -35,8 +39,8 @@ static int write_file(const char* prefix, const char* ext, const void* p, size_t
 }
 
 int main(int argc, char** argv) {
-  if (argc != 5) {
-    fprintf(stderr, "usage: %s rows cols input.bin prefix\n", argv[0]);
+  if (argc < 5 || argc == 6) {
+    fprintf(stderr, "usage: %s rows cols input.bin prefix [offsets...]\n", argv[0]);
     return 1;
   }
   const int64_t rows = atoll(argv[1]), cols = atoll(argv[2]);
@@ -45,6 +49,14 @@ int main(int argc, char** argv) {
     return 1;
   }
   const size_t n = (size_t)rows * (size_t)cols;
+  const int64_t n_experts = argc > 5 ? argc - 6 : 0;
+  int64_t* offsets = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_experts + 1));
+  for (int64_t e = 0; e <= n_experts && n_experts > 0; ++e) offsets[e] = atoll(argv[5 + e]);
+  const int64_t ld_q8 = (rows + 15) / 16 * 16, ld_s = (rows + 127 * n_experts) / 128;
+  const size_t fc_sizes[3] = {(size_t)cols * (size_t)ld_q8, (size_t)cols * (size_t)ld_s * sizeof(float),
+                              sizeof(int64_t) * (size_t)(n_experts + 1)};
+  void* dfc[3] = {0, 0, 0};  /* FP8 columns, their scales, the offsets */
+  uint8_t* fc_host[2] = {0, 0};
   const size_t sizes[5] = {n * 2, n / 2, n / 32, n / 2, n / 32};  /* x, codes/scales row, codes/scales col */
   uint8_t* host[5];
   int have = 1;
@@ -57,6 +69,7 @@ int main(int argc, char** argv) {
     fprintf(stderr, "cannot read %zu bytes from %s\n", sizes[0], argv[3]);
     for (int i = 0; i < 5; ++i) free(host[i]);
     free(deq);
+    free(offsets);
     return 1;
   }
 
@@ -70,6 +83,11 @@ int main(int argc, char** argv) {
   if (ok) ok = hip_ok(hipMalloc(&ddeq, n * 2), "hipMalloc");
   for (int i = 0; i < 3 && ok; ++i) ok = hip_ok(hipMalloc(&dnv[i], nv_sizes[i]), "hipMalloc");
   for (int i = 0; i < 3 && ok; ++i) ok = (nv_host[i] = (uint8_t*)malloc(nv_sizes[i])) != NULL;
+  if (n_experts > 0) {
+    for (int i = 0; i < 3 && ok; ++i) ok = hip_ok(hipMalloc(&dfc[i], fc_sizes[i]), "hipMalloc");
+    for (int i = 0; i < 2 && ok; ++i) ok = (fc_host[i] = (uint8_t*)malloc(fc_sizes[i])) != NULL;
+    if (ok) ok = hip_ok(hipMemcpy(dfc[2], offsets, fc_sizes[2], hipMemcpyHostToDevice), "hipMemcpy offsets");
+  }
   if (ok) ok = hip_ok(hipMemcpy(dev[0], host[0], sizes[0], hipMemcpyHostToDevice), "hipMemcpy in");
   if (ok) {
     /* a null stream: the device's default stream */
@@ -83,6 +101,11 @@ int main(int argc, char** argv) {
     if (s == MXQ_OK)
       s = mxq_quantize(dev[0], MXQ_BF16, rows, cols, cols, MXQ_NVFP4, MXQ_ROWWISE, MXQ_RNE, 0, 0,
                        (uint8_t*)dnv[0], (uint8_t*)dnv[1], NULL, NULL, NULL, (float*)dnv[2], NULL);
+    /* the MXFP4 rows just written, as FP8 columns per expert group */
+    if (s == MXQ_OK && n_experts > 0)
+      s = mxq_fp4_row_to_fp8_col((const uint8_t*)dev[1], (const uint8_t*)dev[2], rows, cols,
+                                 (const int64_t*)dfc[2], n_experts, (uint8_t*)dfc[0], ld_q8, (float*)dfc[1],
+                                 ld_s, NULL);
     if (s != MXQ_OK) {
       fprintf(stderr, "libmxq: %s\n", mxq_status_string(s));
       ok = 0;
@@ -96,8 +119,12 @@ int main(int argc, char** argv) {
   for (int i = 0; i < 5; ++i)
     if (dev[i]) hipFree(dev[i]);
   if (ddeq) hipFree(ddeq);
+  for (int i = 0; i < 2 && ok && n_experts > 0; ++i)
+    ok = hip_ok(hipMemcpy(fc_host[i], dfc[i], fc_sizes[i], hipMemcpyDeviceToHost), "hipMemcpy out");
   for (int i = 0; i < 3; ++i)
     if (dnv[i]) hipFree(dnv[i]);
+  for (int i = 0; i < 3; ++i)
+    if (dfc[i]) hipFree(dfc[i]);
 
   int status = ok ? 0 : 2;
   const char* ext[5] = {"", "codes_row", "scales_row", "codes_col", "scales_col"};
@@ -107,6 +134,11 @@ int main(int argc, char** argv) {
   const char* nv_ext[3] = {"nv_codes", "nv_scales", "nv_st"};
   for (int i = 0; i < 3 && status == 0; ++i)
     if (!write_file(argv[4], nv_ext[i], nv_host[i], nv_sizes[i])) status = 1;
+  const char* fc_ext[2] = {"fc_q8", "fc_s"};
+  for (int i = 0; i < 2 && status == 0 && n_experts > 0; ++i)
+    if (!write_file(argv[4], fc_ext[i], fc_host[i], fc_sizes[i])) status = 1;
+  for (int i = 0; i < 2; ++i) free(fc_host[i]);
+  free(offsets);
   for (int i = 0; i < 3; ++i) free(nv_host[i]);
   for (int i = 0; i < 5; ++i) free(host[i]);
   free(deq);

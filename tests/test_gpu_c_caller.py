@@ -1,9 +1,10 @@
 """The C ABI from a plain C program: tests/c_caller/mxq_c_caller.c is compiled with
 gcc against include/mxq.h and the HIP runtime (no PyTorch, no Python binding), reads
 a seeded bf16 tensor from a file into memory from hipMalloc, quantises it to MXFP4
-row- and column-wise in one call, dequantises the rows, and quantises it to NVFP4
-with no amax given (the library computes the tensor amax first); every output is
-compared with the oracle bit for bit."""
+row- and column-wise in one call, dequantises the rows, quantises it to NVFP4 with no
+amax given (the library computes the tensor amax first), and converts the MXFP4 rows
+to FP8 columns per 128-token group of ragged experts; every output is compared with
+the oracle bit for bit."""
 import os
 import shutil
 import subprocess
@@ -14,7 +15,7 @@ import torch
 
 from gpu_helpers import assert_equal_bits, require_gpu
 from mxfp4_microscaling_quantization_amd import workloads
-from oracle import mx, nvfp4
+from oracle import fp8, mx, nvfp4
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +39,10 @@ def build(tmp):
     return exe
 
 
+# expert token offsets (ragged, one expert of a single token)
+OFFSETS = {96: [0, 40, 41, 96], 1024: [0, 100, 300, 301, 1024]}
+
+
 @pytest.mark.parametrize("rows,cols", [(96, 544), (1024, 4096)])
 def test_c_program_matches_oracle(tmp_path, rows, cols):
     require_gpu()
@@ -47,7 +52,9 @@ def test_c_program_matches_oracle(tmp_path, rows, cols):
     x.view(torch.int16).numpy().tofile(src)
     prefix = os.path.join(str(tmp_path), "out")
     print(f"C caller {rows}x{cols}", flush=True)
-    r = subprocess.run([exe, str(rows), str(cols), src, prefix], capture_output=True, text=True, timeout=120)
+    off = OFFSETS[rows]
+    r = subprocess.run([exe, str(rows), str(cols), src, prefix, *map(str, off)], capture_output=True, text=True,
+                       timeout=120)
     assert r.returncode == 0, r.stderr
     got = {k: np.fromfile(f"{prefix}.{k}", dtype=np.uint8)
            for k in ("codes_row", "scales_row", "codes_col", "scales_col")}
@@ -67,3 +74,9 @@ def test_c_program_matches_oracle(tmp_path, rows, cols):
                       "C caller: NVFP4 block scales (NULL amax)")
     assert_equal_bits(np.fromfile(f"{prefix}.nv_codes", dtype=np.uint8).reshape(rows, cols // 2), nv_c,
                       "C caller: NVFP4 codes (NULL amax)")
+    ref_q8, ref_sb = fp8.mxfp4_rows_to_fp8_cols(ref_c, ref_s, np.array(off, dtype=np.int64))
+    ld_q8, ld_s, groups = (rows + 15) // 16 * 16, (rows + 127 * (len(off) - 1)) // 128, ref_sb.shape[1]
+    q8 = np.fromfile(f"{prefix}.fc_q8", dtype=np.uint8).reshape(cols, ld_q8)[:, :rows]
+    sb = np.fromfile(f"{prefix}.fc_s", dtype=np.uint32).reshape(cols, ld_s)[:, :groups]
+    assert_equal_bits(q8, ref_q8, "C caller: FP8 columns")
+    assert_equal_bits(sb, ref_sb, "C caller: FP8 column scales")
